@@ -1,0 +1,145 @@
+"""Pins for the oracle's combine and its bf16 rounding (CPU only).
+
+Combine (page "[Not ready] MSCCLPP EP implementation #852": combine gathers
+the expert outputs back to each source token and sums them weighted by
+topk_weights, consuming the receiver-side layout that dispatch produced).
+Independent references: torch's CPU fp32->bf16 cast (library routine), exact
+closed forms (weight 1, power-of-two weights), the classical error bound of a
+k-term fp32 fused multiply-add chain against an exact fp64 sum, and the round
+trip dispatch -> identity experts -> combine = x * sum(w).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_get_dispatch_02_amd.workloads import (CONFIGS, expert_outputs, make_workload,
+                                                   mask_slots)
+
+
+def _f32(bits):
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32)
+
+
+def torch_bf16(v):
+    return torch.from_numpy(np.asarray(v, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_rne_matches_torch():
+    rng = np.random.default_rng(3)
+    u = rng.integers(0, 2 ** 32, size=300000, dtype=np.uint64).astype(np.uint32)
+    v = u.view(np.float32)
+    v = v[np.isfinite(v)]
+    # exact ties with both parities of the kept bit, and carries into the exponent
+    ties = (rng.integers(0, 2 ** 16, size=5000).astype(np.uint32) << 16) | 0x8000
+    edge = np.uint32([0x3F7FFFFF, 0x3F7F8000, 0x3F808000, 0x3F818000, 0x7F7FFFFF, 0x7F7F8000,
+                      0x00008000, 0x00018000, 0x80008000, 0x00000001, 0xFF7FFFFF])
+    allv = np.concatenate([v, ties.view(np.float32), edge.view(np.float32)])
+    allv = allv[~np.isnan(allv)]
+    np.testing.assert_array_equal(oracle.bf16_rne(allv), torch_bf16(allv))
+
+
+def test_weight_one_k1_returns_rows():
+    wl = CONFIGS["tiny"].scaled(T=40)
+    wl = dataclasses.replace(wl, k=1)
+    x, idx, w = make_workload(wl)
+    w = np.ones_like(w)
+    d = oracle.dispatch(x, idx, w, wl.E, wl.R)
+    out = oracle.combine(d["recv_x"], d["token_row"], w)
+    np.testing.assert_array_equal(out, x)
+
+
+@pytest.mark.parametrize("k,wv", [(2, 0.5), (4, 0.25), (8, 0.125)])
+def test_power_of_two_weights_identity_experts_exact(k, wv):
+    wl = CONFIGS["dsv3"].scaled(T=33, H=64)
+    wl = dataclasses.replace(wl, k=k)
+    x, idx, _ = make_workload(wl)
+    w = np.full((wl.T, k), wv, np.float32)
+    d = oracle.dispatch(x, idx, w, wl.E, wl.R)
+    out = oracle.combine(d["recv_x"], d["token_row"], w)
+    np.testing.assert_array_equal(out, x)      # every partial sum is exact in fp32
+
+
+def test_identity_experts_give_x_times_sum_w():
+    """Round trip: identity experts make out = bf16(x * fl(sum w)); with softmax
+    weights fl(sum w) is within k*2^-24 of 1, so out is x to within one bf16 ulp."""
+    wl = CONFIGS["dsv3"].scaled(T=64, H=256)
+    x, idx, w = make_workload(wl)
+    d = oracle.dispatch(x, idx, w, wl.E, wl.R)
+    out = oracle.combine(d["recv_x"], d["token_row"], w)
+    xs, os_ = _f32(x).astype(np.float64), _f32(out).astype(np.float64)
+    sw = w.astype(np.float64).sum(1, keepdims=True)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(xs * sw), 1e-38))) - 7)
+    assert np.all(np.abs(os_ - xs * sw) <= ulp * (1 + 1e-6))
+    assert np.mean(out == x) > 0.9
+
+
+def _exact_and_bound(y, trow, w, num_rows):
+    yf = _f32(y).astype(np.float64)
+    T, k = trow.shape
+    H = y.shape[1]
+    S = np.zeros((T, H))
+    A = np.zeros((T, H))
+    for j in range(k):
+        r = trow[:, j]
+        ok = (r >= 0) & (r < num_rows)
+        term = np.where(ok[:, None], w[:, j:j + 1].astype(np.float64) * yf[np.where(ok, r, 0)], 0.0)
+        S += term
+        A += np.abs(term)
+    return S, A
+
+
+@pytest.mark.parametrize("name,mask", [("tiny", 0.0), ("skewed", 0.15), ("dsv3", 0.0)])
+def test_random_experts_within_fma_chain_bound(name, mask):
+    """|bf16(chain) - S| <= 2^-8 (|S| + g A) + g A, g = k 2^-24 / (1 - k 2^-24):
+    fp32 fma-chain error plus one bf16 rounding; catches a dropped, repeated,
+    mis-weighted or sign-flipped term."""
+    wl = CONFIGS[name].scaled(T=48, H=128)
+    x, idx, w = make_workload(wl, seed_extra=5)
+    idx = mask_slots(idx, mask, 1)
+    d = oracle.dispatch(x, idx, w, wl.E, wl.R)
+    N = d["recv_expert_offset"][-1]
+    y = expert_outputs(wl, wl.T * wl.k, seed_extra=1)
+    # random signed weights too, so cancellation is exercised
+    w2 = np.random.default_rng(9).standard_normal(w.shape).astype(np.float32)
+    for ww in (w, w2):
+        out = oracle.combine(y, d["token_row"], ww, num_rows=N)
+        S, A = _exact_and_bound(y, d["token_row"], ww, N)
+        g = wl.k * 2.0 ** -24 / (1 - wl.k * 2.0 ** -24)
+        err = np.abs(_f32(out).astype(np.float64) - S)
+        assert np.all(err <= 2.0 ** -8 * (np.abs(S) + g * A) + g * A + 1e-40)
+
+
+def test_library_cross_check_torch_fp32():
+    wl = CONFIGS["skewed"].scaled(T=64, H=256)
+    x, idx, w = make_workload(wl)
+    d = oracle.dispatch(x, idx, w, wl.E, wl.R)
+    y = expert_outputs(wl, wl.T * wl.k)
+    out = oracle.combine(y, d["token_row"], w)
+    yt = torch.from_numpy(y.view(np.int16)).view(torch.bfloat16).float()
+    ref = (torch.from_numpy(w)[..., None] * yt[torch.from_numpy(d["token_row"]).long()]).sum(1)
+    ref_b = ref.to(torch.bfloat16).float().numpy()
+    o = _f32(out)
+    rel = np.abs(o - ref_b) / np.maximum(np.abs(ref_b), 1e-6)
+    assert np.max(np.abs(o - ref_b)) <= 2 ** -7 * np.abs(ref.numpy()).max()
+    assert np.mean(rel < 8e-3) > 0.99
+
+
+def test_masked_and_out_of_range_rows_skipped():
+    y = np.zeros((4, 8), np.uint16)
+    y[:] = torch_bf16(np.float32([[1.0], [2.0], [4.0], [8.0]]) * np.ones((1, 8), np.float32))
+    trow = np.array([[0, -1, 2], [-1, -1, -1], [3, 4, 1]], np.int32)   # row 4 >= num_rows
+    w = np.array([[1.0, 100.0, 0.5], [1.0, 1.0, 1.0], [0.25, 100.0, 2.0]], np.float32)
+    out = oracle.combine(y, trow, w, num_rows=4)
+    np.testing.assert_array_equal(_f32(out[0]), 3.0)          # 1*1 + 0.5*4
+    np.testing.assert_array_equal(out[1], 0x0000)             # no valid slot: +0
+    np.testing.assert_array_equal(_f32(out[2]), 6.0)          # 0.25*8 + 2*2
+
+
+def test_signed_zero_start():
+    # acc starts at +0: a product of -0 added to +0 gives +0 (fma(-1, 0, +0) = +0)
+    y = np.full((1, 8), 0x0000, np.uint16)
+    out = oracle.combine(y, np.array([[0]], np.int32), np.array([[-1.0]], np.float32))
+    assert np.all(out == 0x0000)
