@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Dispatch + combine throughput of libep.so on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic
+input already resident in HBM:
+    ep_get_dispatch_layout -> ep_dispatch -> ep_combine -> ep_dispatch_fp8
+with the combine fed the dispatched rows (identity experts).  A 512 MiB
+write between phases evicts L2 and the Infinity Cache, standing in for the
+expert computation that sits between dispatch and combine in a real model;
+it is outside every timed phase.
+
+Each phase is bracketed by HIP events recorded on the stream the kernels are
+launched on (torch's current stream, which the binding passes to the C ABI).
+The headline `value` is
+
+    (algorithmic bytes of ep_dispatch + ep_combine) / (t_dispatch + t_combine)
+
+in GB/s, summed over the timed steps.  `roofline` reports the combine kernel
+(one kernel per ep_combine call) against the 8 TB/s HBM3E peak; `traffic`
+comes from committed rocprofv3 FETCH_SIZE / WRITE_SIZE counters when they
+were taken on the current kernel source, else null.  `cpu_baseline` times
+the C oracle (single thread) on the same workload on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine effective GB/s and % of HBM peak at T=4096,H=7168,k=8"
+HBM_PEAK_GBS = 8000.0
+FLUSH_BYTES = 512 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_dsv3_traffic.json")
+COMBINE_SRC = os.path.join(ROOT, "combine_get_dispatch_02_amd", "csrc", "combine.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl):
+    """Bytes each call must move at least (read once, write once)."""
+    T, H, k, E, R, G = wl.T, wl.H, wl.k, wl.E, wl.R, wl.G
+    N = T * k
+    maps = 4 * N + 4 * N + 4 * T * k + 4 * (E + 1) + 4 * (R + 1)   # src, recv_w, token_row, offsets
+    reads = 8 * T * k + 4 * T * k                                  # topk_idx, topk_weights
+    return dict(
+        layout=8 * T * k + T * R + 4 * (E + R + G),
+        dispatch=reads + 2 * T * H + 2 * N * H + maps,
+        dispatch_fp8=reads + 2 * T * H + N * H + 4 * N * (H // 128) + maps,
+        combine=4 * T * k + 4 * T * k + 2 * N * H + 2 * T * H,
+    )
+
+
+def sha_of(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(per_launch_alg_bytes):
+    """Counter-derived HBM bytes of one combine launch, if taken on this source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != sha_of(COMBINE_SRC):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, x, idx, w, budget_s):
+    """Single-threaded C oracle on the same workload: dispatch + combine
+    (identity experts), repeated until the time budget is used."""
+    import ctypes
+
+    import numpy as np
+    import oracle
+
+    L = oracle._load()
+    T, H, k, E, R = wl.T, wl.H, wl.k, wl.E, wl.R
+    N = T * k
+    recv = np.empty((N, H), np.uint16)
+    src = np.empty(N, np.int32)
+    rw = np.empty(N, np.float32)
+    eoff = np.empty(E + 1, np.int32)
+    roff = np.empty(R + 1, np.int32)
+    trow = np.empty((T, k), np.int32)
+    out = np.empty((T, H), np.uint16)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    t_d = t_c = 0.0
+    passes = 0
+    t_start = time.perf_counter()
+    while passes == 0 or time.perf_counter() - t_start < budget_s:
+        t0 = time.perf_counter()
+        rc = L.oracle_dispatch(p(x), p(idx), p(w), T, H, k, E, R, p(recv), p(src), p(rw), p(eoff),
+                               p(roff), p(trow))
+        t1 = time.perf_counter()
+        rc |= L.oracle_combine(p(recv), N, p(trow), p(w), T, H, k, p(out))
+        t2 = time.perf_counter()
+        if rc:
+            raise RuntimeError("oracle failed")
+        t_d += t1 - t0
+        t_c += t2 - t1
+        passes += 1
+    b = algorithmic_bytes(wl)
+    gbs = (b["dispatch"] + b["combine"]) * passes / (t_d + t_c) / 1e9
+    try:
+        model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+    except Exception:
+        model = "unknown"
+    return {
+        "value": round(gbs, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{wl.describe()}: {passes} full passes of oracle dispatch + combine "
+                   f"(identity experts), {t_d + t_c:.1f} s, 1 thread"),
+        "dispatch_ms": round(1e3 * t_d / passes, 2),
+        "combine_ms": round(1e3 * t_c / passes, 2),
+        "host_cores_available": len(os.sched_getaffinity(0)),
+        "host_cpu": model,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict caches between phases")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "every destination rank is a partition of one GPU's HBM here; run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from combine_get_dispatch_02_amd import ep
+    from combine_get_dispatch_02_amd.workloads import CONFIGS, make_workload
+
+    wl = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] {wl.describe()} steps={args.steps} warmup={args.warmup} ({ep.version()})")
+    x, idx, w = make_workload(wl)
+    xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    idxd = torch.from_numpy(idx).to(dev)
+    wd = torch.from_numpy(w).to(dev)
+    T, H, k, E, R, P, G = wl.T, wl.H, wl.k, wl.E, wl.R, wl.P, wl.G
+    N = T * k
+
+    # All outputs and workspaces allocated once, outside the timed region.
+    lay = dict(num_tokens_per_rank=torch.empty(R, dtype=torch.int32, device=dev),
+               num_tokens_per_group=torch.empty(G, dtype=torch.int32, device=dev),
+               num_tokens_per_expert=torch.empty(E, dtype=torch.int32, device=dev),
+               is_token_in_rank=torch.empty((T, R), dtype=torch.uint8, device=dev))
+    ws_l = torch.empty(ep.ep_layout_workspace_bytes(T, E, R, P), dtype=torch.uint8, device=dev)
+
+    def maps():
+        return dict(recv_src_idx=torch.empty(N, dtype=torch.int32, device=dev),
+                    recv_topk_weights=torch.empty(N, dtype=torch.float32, device=dev),
+                    recv_expert_offset=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                    recv_rank_offset=torch.empty(R + 1, dtype=torch.int32, device=dev),
+                    token_row=torch.empty((T, k), dtype=torch.int32, device=dev))
+    disp = maps()
+    disp["recv_x"] = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    fp8 = maps()
+    fp8["recv_x_fp8"] = torch.empty((N, H), dtype=torch.uint8, device=dev)
+    fp8["recv_scales"] = torch.empty((N, H // 128), dtype=torch.float32, device=dev)
+    ws_d = torch.empty(ep.ep_dispatch_workspace_bytes(T, k, E), dtype=torch.uint8, device=dev)
+    comb = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
+    phases = ["layout", "dispatch", "combine", "dispatch_fp8"]
+
+    def flush(i):
+        if not args.no_flush:
+            flush_buf.fill_(i & 0xFF)
+
+    def step(i, ev):
+        flush(i)
+        ev[0].record()
+        ep.ep_get_dispatch_layout(idxd, E, R, P, out=lay, workspace=ws_l)
+        ev[1].record()
+        ep.ep_dispatch(xd, idxd, wd, E, R, out=disp, workspace=ws_d)
+        ev[2].record()
+        flush(i + 1)
+        ev[3].record()
+        ep.ep_combine(disp["recv_x"], disp["token_row"], wd, num_rows=N, out=comb)
+        ev[4].record()
+        flush(i + 2)
+        ev[5].record()
+        ep.ep_dispatch_fp8(xd, idxd, wd, E, R, out=fp8, workspace=ws_d)
+        ev[6].record()
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+
+    for i in range(args.warmup):
+        step(i, events())
+    torch.cuda.synchronize()
+    if disp["recv_expert_offset"][-1].item() != N:
+        raise RuntimeError("dispatch filled an unexpected number of rows")
+
+    evs = [events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms = {p: np.array([e[a].elapsed_time(e[b]) for e in evs])
+          for p, (a, b) in zip(phases, [(0, 1), (1, 2), (3, 4), (5, 6)])}
+    B = algorithmic_bytes(wl)
+    t_dc = float(ms["dispatch"].sum() + ms["combine"].sum()) / 1e3
+    value = (B["dispatch"] + B["combine"]) * args.steps / t_dc / 1e9
+    step_ms = float(sum(ms[p].mean() for p in phases))
+    phase_info = {}
+    for p in phases:
+        us = ms[p] * 1e3
+        gbs = B[p] / (us.mean() * 1e-6) / 1e9
+        phase_info[p] = {"us_mean": round(float(us.mean()), 2), "us_median": round(float(np.median(us)), 2),
+                         "us_p10": round(float(np.percentile(us, 10)), 2),
+                         "us_p90": round(float(np.percentile(us, 90)), 2),
+                         "alg_bytes": int(B[p]), "GBps": round(gbs, 1),
+                         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    c_us = float(ms["combine"].mean()) * 1e3
+    achieved = B["combine"] / (c_us * 1e-6) / 1e9
+    traffic = load_traffic(B["combine"])
+    roofline = {"kernel": "combine_kernel (ep_combine)", "bound": "hbm",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "alg_bytes_per_launch": int(B["combine"]), "avg_launch_us": round(c_us, 2)}
+
+    cpu = None
+    if not args.skip_cpu_baseline:
+        log(f"[bench] cpu baseline (oracle, ~{args.cpu_baseline_seconds:.0f} s)")
+        cpu = cpu_baseline(wl, x, idx, w, args.cpu_baseline_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.describe(), "T": T, "H": H, "k": k, "num_experts": E,
+                   "num_ranks": R, "ranks_per_group": P, "global_batch": T, "parallelism": "none (1 GPU)"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "caches_flushed_between_phases": not args.no_flush,
+        "wall_ms_per_step_incl_flush": round(1e3 * wall / args.steps, 4),
+        "phases": phase_info,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

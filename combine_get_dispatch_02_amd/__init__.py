@@ -1,0 +1,13 @@
+"""MI355X-native MoE expert-parallel dispatch / combine.
+
+The computation lives in libep.so (hand-written gfx950 HIP kernels behind the
+C ABI of include/ep.h).  This package holds its thin Python binding
+(:mod:`.ep`), the hipcc build step (:mod:`.build`) and the seeded synthetic
+workload generator (:mod:`.workloads`).
+"""
+from .ep import (EPError, ep_combine, ep_dispatch, ep_dispatch_fp8,  # noqa: F401
+                 ep_dispatch_workspace_bytes, ep_get_dispatch_layout,
+                 ep_layout_workspace_bytes, lib, version)
+
+__all__ = ["EPError", "ep_get_dispatch_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_combine",
+           "ep_layout_workspace_bytes", "ep_dispatch_workspace_bytes", "lib", "version"]

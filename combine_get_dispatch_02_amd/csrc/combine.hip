@@ -1,0 +1,119 @@
+// combine.hip -- ep_combine on gfx950.
+//
+// Page "[Not ready] MSCCLPP EP implementation #852": intranode combine (PR
+// body, "Scope / Intranode") brings every expert output back to its source
+// token and sums them weighted by topk_weights; the commit fixing internode
+// HT combine states that combine must follow the receiver-side layout that
+// dispatch produced -- here token_row[t, j].
+//
+// One wave per (token, column tile).  The wave reads the token's k rows
+// (KB rows of U 16-byte vectors per lane in flight at once), accumulates
+// acc = fma(w[t,j], y[row(t,j)], acc) in fp32 for j = 0..k-1 in that fixed
+// order (v_fma_f32, one rounding per step), and stores bf16 rounded to
+// nearest even.  The result is therefore independent of the launch shape.
+#include "ep_device.h"
+#include "ep_launch.h"
+
+namespace ep {
+namespace {
+
+__device__ __forceinline__ int64_t wave_index() {
+    return static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) +
+           __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+}
+
+template <int U, int KB>
+__global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ y,
+                                                      int64_t num_rows,
+                                                      const int32_t* __restrict__ token_row,
+                                                      const float* __restrict__ topk_weights,
+                                                      u32x4* __restrict__ out, int V, int k,
+                                                      int tiles_per_token, int64_t num_tiles) {
+    const int lane = lane_id();
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (blockDim.x / kWave);
+    for (int64_t tile = wave_index(); tile < num_tiles; tile += nwaves) {
+        const int64_t t = tile / tiles_per_token;
+        const int v0 = static_cast<int>(tile - t * tiles_per_token) * (U * kWave) + lane;
+        int my_row = -1;
+        float my_w = 0.0f;
+        if (lane < k) {
+            my_row = token_row[t * k + lane];
+            my_w = topk_weights[t * k + lane];
+            if (my_row < 0 || static_cast<int64_t>(my_row) >= num_rows) my_row = -1;
+        }
+        float acc[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
+
+        for (int j0 = 0; j0 < k; j0 += KB) {
+            u32x4 val[KB][U];
+            int rows[KB];
+#pragma unroll
+            for (int jj = 0; jj < KB; ++jj) {
+                const int j = j0 + jj;
+                rows[jj] = j < k ? read_lane(my_row, j) : -1;
+                if (rows[jj] >= 0) {
+                    const u32x4* src = y + static_cast<int64_t>(rows[jj]) * V;
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int v = v0 + u * kWave;
+                        val[jj][u] = v < V ? __builtin_nontemporal_load(src + v) : u32x4{0u, 0u, 0u, 0u};
+                    }
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < KB; ++jj) {
+                if (rows[jj] < 0) continue;
+                const float wj = read_lane(my_w, j0 + jj);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[u][2 * i] = __builtin_fmaf(wj, bf16_lo(val[jj][u][i]), acc[u][2 * i]);
+                        acc[u][2 * i + 1] = __builtin_fmaf(wj, bf16_hi(val[jj][u][i]), acc[u][2 * i + 1]);
+                    }
+            }
+        }
+        u32x4* dst = out + t * V;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * kWave;
+            if (v < V) {
+                u32x4 o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    o[i] = bf16_rne(acc[u][2 * i]) | (bf16_rne(acc[u][2 * i + 1]) << 16);
+                __builtin_nontemporal_store(o, dst + v);
+            }
+        }
+    }
+}
+
+template <int U, int KB>
+hipError_t launch_u(const void* y, int64_t num_rows, const int32_t* token_row, const float* w,
+                    void* out, int64_t T, int V, int k, hipStream_t stream) {
+    const int tiles_per_token = static_cast<int>(ceil_div(V, U * kWave));
+    const int64_t num_tiles = T * tiles_per_token;
+    const int64_t blocks = ceil_div(num_tiles, 4);
+    const unsigned grid = static_cast<unsigned>(blocks < (1 << 30) ? blocks : (1 << 30));
+    hipLaunchKernelGGL((combine_kernel<U, KB>), dim3(grid), dim3(256), 0, stream,
+                       static_cast<const u32x4*>(y), num_rows, token_row, w,
+                       static_cast<u32x4*>(out), V, k, tiles_per_token, num_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* expert_out, int64_t num_rows, const int32_t* token_row,
+                          const float* topk_weights, int64_t T, int H, int k, void* out,
+                          hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const int V = H / 8;
+    if (V % (2 * kWave) == 0 && T * (V / (2 * kWave)) >= 4096)
+        return launch_u<2, 8>(expert_out, num_rows, token_row, topk_weights, out, T, V, k, stream);
+    return launch_u<1, 8>(expert_out, num_rows, token_row, topk_weights, out, T, V, k, stream);
+}
+
+}  // namespace ep

@@ -1,0 +1,346 @@
+// dispatch.hip -- receive order and data movement of ep_dispatch /
+// ep_dispatch_fp8 on gfx950.
+//
+// Page "[Not ready] MSCCLPP EP implementation #852": intranode dispatch
+// (PR body, "Scope / Intranode") places each token's hidden vector in the
+// receive buffers of the ranks its experts live on; the low-latency dispatch
+// (low-latency port commit, dispatch<kUseFP8,...>) optionally casts each
+// token to FP8 with one scale per 128 channels on the way.  On one GPU the
+// ranks are contiguous ranges of one receive buffer, rows grouped by expert
+// and, inside an expert, ordered by (token, slot).
+//
+// Kernels (all deterministic; no global atomics):
+//   chunk_hist   per 256-token chunk, per-expert slot counts (LDS atomics)
+//   rows         per chunk: per-expert prefix over earlier chunks + block
+//                scan over experts -> chunk base rows; then the stable rank of
+//                every slot inside the chunk from wave64 ballot matching;
+//                writes token_row, recv_src_idx, recv_topk_weights, offsets
+//   copy_bf16    one wave per (token, column tile): 16-byte loads of x[t]
+//                once, 16-byte non-temporal stores into each of its k rows
+//   copy_fp8     same walk; per 128-channel block amax over 8 lanes, scale
+//                amax/448, E4M3FN codes, 16-byte code stores + scale stores
+#include "ep_device.h"
+#include "ep_launch.h"
+
+namespace ep {
+namespace {
+
+constexpr int kIndexWaves = kIndexThreads / kWave;
+
+__global__ __launch_bounds__(kIndexThreads) void chunk_hist_kernel(
+    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int32_t* __restrict__ hist) {
+    extern __shared__ int32_t h[];
+    for (int e = threadIdx.x; e < E; e += kIndexThreads) h[e] = 0;
+    __syncthreads();
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kChunkTokens;
+    const int64_t t1 = t0 + kChunkTokens < T ? t0 + kChunkTokens : T;
+    for (int64_t s = t0 * k + threadIdx.x; s < t1 * k; s += kIndexThreads) {
+        const int64_t e = topk_idx[s];
+        if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+    }
+    __syncthreads();
+    int32_t* out = hist + static_cast<int64_t>(blockIdx.x) * E;
+    for (int e = threadIdx.x; e < E; e += kIndexThreads) out[e] = h[e];
+}
+
+// In-place exclusive scan of a[0..n) held in LDS, n <= 8 * kIndexThreads.
+// Every thread gets the total.  Caller synchronises before; this syncs after.
+__device__ int block_exclusive_scan(int32_t* a, int n, int32_t* wave_tot) {
+    const int ipt = (n + kIndexThreads - 1) / kIndexThreads;
+    const int b = threadIdx.x * ipt;
+    int sum = 0;
+    for (int i = 0; i < ipt; ++i)
+        if (b + i < n) sum += a[b + i];
+    int incl = sum;
+    const int lane = lane_id();
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int v = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += v;
+    }
+    const int wave = threadIdx.x / kWave;
+    if (lane == kWave - 1) wave_tot[wave] = incl;
+    __syncthreads();
+    int base = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kIndexWaves; ++w) {
+        base += (w < wave) ? wave_tot[w] : 0;
+        total += wave_tot[w];
+    }
+    int run = base + incl - sum;
+    for (int i = 0; i < ipt; ++i)
+        if (b + i < n) {
+            const int v = a[b + i];
+            a[b + i] = run;
+            run += v;
+        }
+    __syncthreads();
+    return total;
+}
+
+__global__ __launch_bounds__(kIndexThreads) void rows_kernel(
+    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int64_t T,
+    int k, int E, int R, int nchunks, int nbits, const int32_t* __restrict__ hist,
+    int32_t* __restrict__ token_row, int32_t* __restrict__ recv_src_idx,
+    float* __restrict__ recv_w, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ rank_offset) {
+    extern __shared__ int32_t lds[];
+    int32_t* base = lds;                          // [E]  first row of (chunk, expert)
+    int32_t* wc = lds + E;                        // [kIndexWaves][E] per-wave cursors
+    int32_t* wave_tot = lds + (1 + kIndexWaves) * E;
+    const int c = blockIdx.x;
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+
+    // 1. Per expert: slots in all chunks (-> base, scanned below) and in the
+    //    chunks before this one (-> wc[0], added after the scan).
+    for (int e = threadIdx.x; e < E; e += kIndexThreads) {
+        int tot = 0, pre = 0;
+        for (int cc = 0; cc < nchunks; ++cc) {
+            const int v = hist[static_cast<int64_t>(cc) * E + e];
+            tot += v;
+            pre += (cc < c) ? v : 0;
+        }
+        base[e] = tot;
+        wc[e] = pre;
+    }
+    __syncthreads();
+    const int total = block_exclusive_scan(base, E, wave_tot);
+    if (c == 0) {
+        const int epr = E / R;
+        for (int e = threadIdx.x; e <= E; e += kIndexThreads) expert_offset[e] = e < E ? base[e] : total;
+        if (rank_offset)
+            for (int r = threadIdx.x; r <= R; r += kIndexThreads)
+                rank_offset[r] = r < R ? base[r * epr] : total;
+    }
+    for (int e = threadIdx.x; e < E; e += kIndexThreads) base[e] += wc[e];
+    __syncthreads();
+
+    // 2. Slots of this chunk, split into kIndexWaves contiguous ranges of Q
+    //    (a multiple of 64) slots; each wave counts its range per expert.
+    const int64_t t0 = static_cast<int64_t>(c) * kChunkTokens;
+    const int64_t s0 = t0 * k;
+    const int nt = static_cast<int>(T - t0 < kChunkTokens ? T - t0 : kChunkTokens);
+    const int S = nt * k;
+    const int Q = (S + kIndexThreads - 1) / kIndexThreads * kWave;
+    for (int i = threadIdx.x; i < kIndexWaves * E; i += kIndexThreads) wc[i] = 0;
+    __syncthreads();
+    int32_t* my = wc + wave * E;
+    for (int i = lane; i < Q; i += kWave) {
+        const int s = wave * Q + i;
+        if (s < S) {
+            const int64_t e = topk_idx[s0 + s];
+            if (e >= 0 && e < E) atomicAdd(&my[e], 1);
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kIndexThreads) {
+        int run = base[e];
+        for (int w = 0; w < kIndexWaves; ++w) {
+            const int v = wc[w * E + e];
+            wc[w * E + e] = run;
+            run += v;
+        }
+    }
+    __syncthreads();
+
+    // 3. Each wave walks its range 64 slots at a time, in order.  A slot's
+    //    row = its wave's cursor for the expert + number of lower lanes with
+    //    the same expert; the highest such lane then advances the cursor.
+    //    (LDS accesses of one wave complete in program order.)
+    for (int g = 0; g < Q; g += kWave) {
+        const int s = wave * Q + g + lane;
+        const bool in = s < S;
+        const int64_t e64 = in ? topk_idx[s0 + s] : -1;
+        const bool valid = in && e64 >= 0 && e64 < E;
+        const int e = valid ? static_cast<int>(e64) : 0;
+        const uint64_t peers = match_key(e, valid, nbits);
+        int row = -1;
+        if (valid) row = my[e] + __popcll(peers & lanes_below());
+        if (valid && (peers >> lane) == 1) my[e] += __popcll(peers);
+        if (in) {
+            const int64_t gs = s0 + s;
+            token_row[gs] = row;
+            if (valid) {
+                recv_src_idx[row] = static_cast<int32_t>(gs / k);
+                if (recv_w) recv_w[row] = topk_weights[gs];
+            }
+        }
+    }
+}
+
+__global__ void zero_offsets_kernel(int32_t* expert_offset, int E, int32_t* rank_offset, int R) {
+    for (int i = threadIdx.x; i <= E; i += blockDim.x) expert_offset[i] = 0;
+    if (rank_offset)
+        for (int i = threadIdx.x; i <= R; i += blockDim.x) rank_offset[i] = 0;
+}
+
+// Wave index made explicitly uniform (an SGPR) so per-tile indices stay scalar.
+__device__ __forceinline__ int64_t wave_index() {
+    return static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) +
+           __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+}
+
+// bf16 copy: tile = (token t, U*64 consecutive 16-byte vectors of its row).
+template <int U>
+__global__ __launch_bounds__(256) void copy_bf16_kernel(const u32x4* __restrict__ x,
+                                                        const int32_t* __restrict__ token_row,
+                                                        u32x4* __restrict__ recv, int V, int k,
+                                                        int tiles_per_token, int64_t num_tiles) {
+    const int lane = lane_id();
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (blockDim.x / kWave);
+    for (int64_t tile = wave_index(); tile < num_tiles; tile += nwaves) {
+        const int64_t t = tile / tiles_per_token;
+        const int v0 = static_cast<int>(tile - t * tiles_per_token) * (U * kWave) + lane;
+        const u32x4* src = x + t * V;
+        u32x4 val[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * kWave;
+            if (v < V) val[u] = __builtin_nontemporal_load(src + v);
+        }
+        const int my_row = lane < k ? token_row[t * k + lane] : -1;
+        for (int j = 0; j < k; ++j) {
+            const int r = read_lane(my_row, j);
+            if (r < 0) continue;
+            u32x4* dst = recv + static_cast<int64_t>(r) * V;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int v = v0 + u * kWave;
+                if (v < V) __builtin_nontemporal_store(val[u], dst + v);
+            }
+        }
+    }
+}
+
+// FP8 copy: a lane owns 16 consecutive channels (two 16-byte bf16 vectors),
+// 8 lanes one 128-channel block, a wave 1024 channels of one token.
+__global__ __launch_bounds__(256) void copy_fp8_kernel(const u32x4* __restrict__ x,
+                                                       const int32_t* __restrict__ token_row,
+                                                       uint8_t* __restrict__ recv_q,
+                                                       float* __restrict__ recv_scales, int H,
+                                                       int k, int tiles_per_token,
+                                                       int64_t num_tiles) {
+    const int lane = lane_id();
+    const int V = H / 8;
+    const int nb = H / 128;
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (blockDim.x / kWave);
+    for (int64_t tile = wave_index(); tile < num_tiles; tile += nwaves) {
+        const int64_t t = tile / tiles_per_token;
+        const int ch0 = static_cast<int>(tile - t * tiles_per_token) * 1024 + lane * 16;
+        const bool active = ch0 < H;
+        u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
+        if (active) {
+            const u32x4* src = x + t * V + ch0 / 8;
+            a0 = __builtin_nontemporal_load(src);
+            a1 = __builtin_nontemporal_load(src + 1);
+        }
+        float f[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = bf16_lo(a0[i]);
+            f[2 * i + 1] = bf16_hi(a0[i]);
+            f[8 + 2 * i] = bf16_lo(a1[i]);
+            f[8 + 2 * i + 1] = bf16_hi(a1[i]);
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+        amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
+        const float s = amax / 448.0f;
+        u32x4 q = {0u, 0u, 0u, 0u};
+        if (s > 0.0f) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) q[i / 4] |= e4m3fn_encode(f[i] / s) << (8 * (i % 4));
+        }
+        const int my_row = lane < k ? token_row[t * k + lane] : -1;
+        for (int j = 0; j < k; ++j) {
+            const int r = read_lane(my_row, j);
+            if (r < 0) continue;
+            if (active) {
+                __builtin_nontemporal_store(
+                    q, reinterpret_cast<u32x4*>(recv_q + static_cast<int64_t>(r) * H + ch0));
+                if ((lane & 7) == 0) recv_scales[static_cast<int64_t>(r) * nb + ch0 / 128] = s;
+            }
+        }
+    }
+}
+
+template <int U>
+hipError_t launch_copy_bf16_u(const void* x, const int32_t* token_row, void* recv, int64_t T,
+                              int V, int k, hipStream_t stream) {
+    const int tiles_per_token = static_cast<int>(ceil_div(V, U * kWave));
+    const int64_t num_tiles = T * tiles_per_token;
+    const int64_t blocks = ceil_div(num_tiles, 4);
+    const unsigned grid = static_cast<unsigned>(blocks < (1 << 30) ? blocks : (1 << 30));
+    hipLaunchKernelGGL(copy_bf16_kernel<U>, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const u32x4*>(x), token_row, static_cast<u32x4*>(recv), V, k,
+                       tiles_per_token, num_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t index_workspace_bytes(int64_t T, int E) {
+    const int64_t nchunks = ceil_div(T, kChunkTokens);
+    const size_t b = static_cast<size_t>(nchunks) * static_cast<size_t>(E) * sizeof(int32_t);
+    return round_up(b > 0 ? b : 1, 256);
+}
+
+hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weights, int64_t T,
+                                 int k, int E, int R, int32_t* recv_src_idx, float* recv_w,
+                                 int32_t* expert_offset, int32_t* rank_offset,
+                                 int32_t* token_row, void* workspace, hipStream_t stream) {
+    if (T == 0) {
+        hipLaunchKernelGGL(zero_offsets_kernel, dim3(1), dim3(256), 0, stream, expert_offset, E,
+                           rank_offset, R);
+        return hipGetLastError();
+    }
+    const int nchunks = static_cast<int>(ceil_div(T, kChunkTokens));
+    int32_t* hist = static_cast<int32_t*>(workspace);
+    hipLaunchKernelGGL(chunk_hist_kernel, dim3(nchunks), dim3(kIndexThreads),
+                       static_cast<size_t>(E) * sizeof(int32_t), stream, topk_idx, T, k, E, hist);
+    const int nbits = E > 1 ? 32 - __builtin_clz(static_cast<unsigned>(E - 1)) : 0;
+    const size_t lds = (static_cast<size_t>(1 + kIndexWaves) * E + kIndexWaves) * sizeof(int32_t);
+    hipLaunchKernelGGL(rows_kernel, dim3(nchunks), dim3(kIndexThreads), lds, stream, topk_idx,
+                       (recv_w ? topk_weights : nullptr), T, k, E, R, nchunks, nbits, hist,
+                       token_row, recv_src_idx, (topk_weights ? recv_w : nullptr), expert_offset,
+                       rank_offset);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_copy_bf16(const void* x, const int32_t* token_row, void* recv_x,
+                                     int64_t T, int H, int k, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const int V = H / 8;
+    // Largest tile (more bytes in flight per wave) that divides the row and
+    // still leaves enough waves to fill 256 CUs.
+    const int64_t want_waves = 4096;
+    if (V % (8 * kWave) == 0 && T * (V / (8 * kWave)) >= want_waves)
+        return launch_copy_bf16_u<8>(x, token_row, recv_x, T, V, k, stream);
+    if (V % (7 * kWave) == 0 && T * (V / (7 * kWave)) >= want_waves)
+        return launch_copy_bf16_u<7>(x, token_row, recv_x, T, V, k, stream);
+    if (V % (4 * kWave) == 0 && T * (V / (4 * kWave)) >= want_waves)
+        return launch_copy_bf16_u<4>(x, token_row, recv_x, T, V, k, stream);
+    if (V % (2 * kWave) == 0 && T * (V / (2 * kWave)) >= want_waves)
+        return launch_copy_bf16_u<2>(x, token_row, recv_x, T, V, k, stream);
+    return launch_copy_bf16_u<1>(x, token_row, recv_x, T, V, k, stream);
+}
+
+hipError_t launch_dispatch_copy_fp8(const void* x, const int32_t* token_row, uint8_t* recv_q,
+                                    float* recv_scales, int64_t T, int H, int k,
+                                    hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const int tiles_per_token = static_cast<int>(ceil_div(H, 1024));
+    const int64_t num_tiles = T * tiles_per_token;
+    const int64_t blocks = ceil_div(num_tiles, 4);
+    const unsigned grid = static_cast<unsigned>(blocks < (1 << 30) ? blocks : (1 << 30));
+    hipLaunchKernelGGL(copy_fp8_kernel, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const u32x4*>(x), token_row, recv_q, recv_scales, H, k,
+                       tiles_per_token, num_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace ep

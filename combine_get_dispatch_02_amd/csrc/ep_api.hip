@@ -1,0 +1,193 @@
+// ep_api.hip -- the C ABI of include/ep.h: argument validation, workspace
+// sizing, status codes, and the launch sequence of every entry point.
+//
+// Validation happens on the host before anything is enqueued, so an invalid
+// call leaves every output untouched and can never make a kernel index out
+// of the buffers described in ep.h.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/ep.h"
+#include "ep_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_status(hipError_t e, const char* where) {
+    if (e == hipSuccess) return EP_OK;
+    return fail(EP_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Routing arguments shared by every entry point that reads topk_idx.
+int check_routing(const char* fn, const int64_t* topk_idx, int64_t T, int k, int E, int R) {
+    if (T < 0) return fail(EP_ERR_INVALID_ARGUMENT, "%s: num_tokens < 0", fn);
+    if (k < 1) return fail(EP_ERR_INVALID_ARGUMENT, "%s: num_topk < 1", fn);
+    if (k > EP_MAX_TOPK) return fail(EP_ERR_UNSUPPORTED, "%s: num_topk > %d", fn, EP_MAX_TOPK);
+    if (E < 1 || R < 1) return fail(EP_ERR_INVALID_ARGUMENT, "%s: num_experts and num_ranks must be >= 1", fn);
+    if (R > EP_MAX_RANKS) return fail(EP_ERR_UNSUPPORTED, "%s: num_ranks > %d", fn, EP_MAX_RANKS);
+    if (E > EP_MAX_EXPERTS) return fail(EP_ERR_UNSUPPORTED, "%s: num_experts > %d", fn, EP_MAX_EXPERTS);
+    if (E % R != 0) return fail(EP_ERR_INVALID_ARGUMENT, "%s: num_experts %% num_ranks != 0", fn);
+    if (T > 0 && !topk_idx) return fail(EP_ERR_INVALID_ARGUMENT, "%s: topk_idx is NULL", fn);
+    if (T * static_cast<int64_t>(k) > INT32_MAX)
+        return fail(EP_ERR_UNSUPPORTED, "%s: num_tokens * num_topk >= 2^31", fn);
+    return EP_OK;
+}
+
+int check_dispatch_common(const char* fn, const void* x, const int64_t* topk_idx, int64_t T,
+                          int H, int k, int E, int R, const void* recv, const int32_t* recv_src_idx,
+                          const int32_t* expert_offset, const int32_t* token_row,
+                          size_t ws_bytes) {
+    int s = check_routing(fn, topk_idx, T, k, E, R);
+    if (s != EP_OK) return s;
+    if (H < 8 || H % 8 != 0) return fail(EP_ERR_INVALID_ARGUMENT, "%s: hidden must be a positive multiple of 8", fn);
+    if (!expert_offset) return fail(EP_ERR_INVALID_ARGUMENT, "%s: recv_expert_offset is NULL", fn);
+    if (T > 0 && (!x || !recv || !recv_src_idx || !token_row))
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: a required pointer is NULL", fn);
+    if (T > 0 && (!aligned16(x) || !aligned16(recv)))
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: x and the receive buffer must be 16-byte aligned", fn);
+    if (T > 0 && ws_bytes < ep::index_workspace_bytes(T, E))
+        return fail(EP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes", fn,
+                    ep::index_workspace_bytes(T, E));
+    return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ep_status_string(int status) {
+    switch (status) {
+        case EP_OK: return "EP_OK";
+        case EP_ERR_INVALID_ARGUMENT: return "EP_ERR_INVALID_ARGUMENT";
+        case EP_ERR_UNSUPPORTED: return "EP_ERR_UNSUPPORTED";
+        case EP_ERR_WORKSPACE_TOO_SMALL: return "EP_ERR_WORKSPACE_TOO_SMALL";
+        case EP_ERR_HIP: return "EP_ERR_HIP";
+        default: return "EP_ERR_UNKNOWN";
+    }
+}
+
+const char* ep_last_error(void) { return g_last_error; }
+
+const char* ep_version(void) { return "ep-mi355x 0.1 gfx950"; }
+
+size_t ep_layout_workspace_bytes(int64_t num_tokens, int num_experts, int num_ranks,
+                                 int ranks_per_group) {
+    if (num_tokens < 0 || num_experts < 1 || num_ranks < 1 || ranks_per_group < 1) return 0;
+    return ep::layout_workspace_bytes(num_tokens, num_experts, num_ranks,
+                                      num_ranks / ranks_per_group);
+}
+
+int ep_get_dispatch_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
+                           int num_experts, int num_ranks, int ranks_per_group,
+                           int32_t* num_tokens_per_rank, int32_t* num_tokens_per_group,
+                           int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "ep_get_dispatch_layout";
+    int s = check_routing(fn, topk_idx, num_tokens, num_topk, num_experts, num_ranks);
+    if (s != EP_OK) return s;
+    if (ranks_per_group < 1 || num_ranks % ranks_per_group != 0)
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: num_ranks %% ranks_per_group != 0", fn);
+    if (!num_tokens_per_rank || !num_tokens_per_expert || (num_tokens > 0 && !is_token_in_rank))
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: a required pointer is NULL", fn);
+    const size_t need = ep::layout_workspace_bytes(num_tokens, num_experts, num_ranks,
+                                                   num_ranks / ranks_per_group);
+    if (num_tokens > 0 && (!workspace || workspace_bytes < need))
+        return fail(EP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes", fn, need);
+    return hip_status(ep::launch_layout(topk_idx, num_tokens, num_topk, num_experts, num_ranks,
+                                        ranks_per_group, num_tokens_per_rank,
+                                        num_tokens_per_group, num_tokens_per_expert,
+                                        is_token_in_rank, workspace,
+                                        static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+size_t ep_dispatch_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts) {
+    if (num_tokens < 0 || num_topk < 1 || num_experts < 1) return 0;
+    return ep::index_workspace_bytes(num_tokens, num_experts);
+}
+
+int ep_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                int64_t num_tokens, int hidden, int num_topk, int num_experts, int num_ranks,
+                void* recv_x, int32_t* recv_src_idx, float* recv_topk_weights,
+                int32_t* recv_expert_offset, int32_t* recv_rank_offset, int32_t* token_row,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "ep_dispatch";
+    int s = check_dispatch_common(fn, x, topk_idx, num_tokens, hidden, num_topk, num_experts,
+                                  num_ranks, recv_x, recv_src_idx, recv_expert_offset, token_row,
+                                  workspace ? workspace_bytes : 0);
+    if (s != EP_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    s = hip_status(ep::launch_dispatch_index(topk_idx, topk_weights, num_tokens, num_topk,
+                                             num_experts, num_ranks, recv_src_idx,
+                                             recv_topk_weights, recv_expert_offset,
+                                             recv_rank_offset, token_row, workspace, st),
+                   fn);
+    if (s != EP_OK) return s;
+    return hip_status(ep::launch_dispatch_copy_bf16(x, token_row, recv_x, num_tokens, hidden,
+                                                    num_topk, st),
+                      fn);
+}
+
+int ep_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                    int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                    int num_ranks, uint8_t* recv_x_fp8, float* recv_scales,
+                    int32_t* recv_src_idx, float* recv_topk_weights,
+                    int32_t* recv_expert_offset, int32_t* recv_rank_offset,
+                    int32_t* token_row, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    const char* fn = "ep_dispatch_fp8";
+    int s = check_dispatch_common(fn, x, topk_idx, num_tokens, hidden, num_topk, num_experts,
+                                  num_ranks, recv_x_fp8, recv_src_idx, recv_expert_offset,
+                                  token_row, workspace ? workspace_bytes : 0);
+    if (s != EP_OK) return s;
+    if (hidden % 128 != 0) return fail(EP_ERR_INVALID_ARGUMENT, "%s: hidden %% 128 != 0", fn);
+    if (num_tokens > 0 && !recv_scales)
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: recv_scales is NULL", fn);
+    if (num_tokens > 0 && (reinterpret_cast<uintptr_t>(recv_scales) & 3u))
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: recv_scales must be 4-byte aligned", fn);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    s = hip_status(ep::launch_dispatch_index(topk_idx, topk_weights, num_tokens, num_topk,
+                                             num_experts, num_ranks, recv_src_idx,
+                                             recv_topk_weights, recv_expert_offset,
+                                             recv_rank_offset, token_row, workspace, st),
+                   fn);
+    if (s != EP_OK) return s;
+    return hip_status(ep::launch_dispatch_copy_fp8(x, token_row, recv_x_fp8, recv_scales,
+                                                   num_tokens, hidden, num_topk, st),
+                      fn);
+}
+
+int ep_combine(const void* expert_out, int64_t num_rows, const int32_t* token_row,
+               const float* topk_weights, int64_t num_tokens, int hidden, int num_topk,
+               void* combined_x, void* stream) {
+    const char* fn = "ep_combine";
+    if (num_tokens < 0 || num_rows < 0)
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: num_tokens and num_rows must be >= 0", fn);
+    if (num_topk < 1) return fail(EP_ERR_INVALID_ARGUMENT, "%s: num_topk < 1", fn);
+    if (num_topk > EP_MAX_TOPK) return fail(EP_ERR_UNSUPPORTED, "%s: num_topk > %d", fn, EP_MAX_TOPK);
+    if (hidden < 8 || hidden % 8 != 0)
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: hidden must be a positive multiple of 8", fn);
+    if (num_tokens > 0 && (!token_row || !topk_weights || !combined_x))
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: a required pointer is NULL", fn);
+    if (num_tokens > 0 && num_rows > 0 && !expert_out)
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: expert_out is NULL", fn);
+    if (num_tokens > 0 && (!aligned16(combined_x) || (num_rows > 0 && !aligned16(expert_out))))
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: expert_out and combined_x must be 16-byte aligned", fn);
+    return hip_status(ep::launch_combine(expert_out, num_rows, token_row, topk_weights,
+                                         num_tokens, hidden, num_topk, combined_x,
+                                         static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// ep_launch.h -- internal kernel launchers of libep.so (host side).
+//
+// The C ABI in include/ep.h validates arguments and then calls these; each
+// launcher only sizes its grid and enqueues on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ep {
+
+// Tokens per block of the layout histogram kernel (one token per thread).
+constexpr int kLayoutTokensPerBlock = 256;
+// Tokens per chunk of the receive-order computation.  Rows are ranked inside
+// a chunk with wave ballots; chunks are chained by per-expert prefix sums.
+constexpr int kChunkTokens = 256;
+constexpr int kIndexThreads = 256;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
+
+// ---- layout -----------------------------------------------------------------
+size_t layout_workspace_bytes(int64_t T, int E, int R, int G);
+hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R, int P,
+                         int32_t* per_rank, int32_t* per_group, int32_t* per_expert,
+                         uint8_t* in_rank, void* workspace, hipStream_t stream);
+
+// ---- receive order (shared by both dispatch variants) -------------------------
+size_t index_workspace_bytes(int64_t T, int E);
+hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weights, int64_t T,
+                                 int k, int E, int R, int32_t* recv_src_idx, float* recv_w,
+                                 int32_t* expert_offset, int32_t* rank_offset,
+                                 int32_t* token_row, void* workspace, hipStream_t stream);
+
+// ---- data movement ------------------------------------------------------------
+hipError_t launch_dispatch_copy_bf16(const void* x, const int32_t* token_row, void* recv_x,
+                                     int64_t T, int H, int k, hipStream_t stream);
+hipError_t launch_dispatch_copy_fp8(const void* x, const int32_t* token_row, uint8_t* recv_q,
+                                    float* recv_scales, int64_t T, int H, int k,
+                                    hipStream_t stream);
+hipError_t launch_combine(const void* expert_out, int64_t num_rows, const int32_t* token_row,
+                          const float* topk_weights, int64_t T, int H, int k, void* out,
+                          hipStream_t stream);
+
+}  // namespace ep

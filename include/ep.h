@@ -1,0 +1,186 @@
+/*
+ * ep.h -- C ABI of the MI355X (gfx950) MoE expert-parallel dispatch / combine
+ * library (libep.so).
+ *
+ * The operations are the expert-parallel hot path of the page
+ * "[Not ready] MSCCLPP EP implementation #852" (microsoft/mscclpp pull 852):
+ *   - get_dispatch_layout (PR body, "Scope / Intranode" and "Internode HT"),
+ *   - dispatch and combine over the x[T,H] bf16 / topk_idx[T,k] int64 /
+ *     topk_weights[T,k] fp32 tensor ABI (same section),
+ *   - the low-latency dispatch with per-token FP8 casting and one scale per
+ *     128 channels (low-latency port commit, dispatch<kUseFP8,...>),
+ *   - combine consuming the receiver-side layout produced by dispatch (commit
+ *     fixing internode HT combine: receiver-side prefix sums).
+ * On one GPU every destination "rank" is a contiguous range of one receive
+ * buffer in this GPU's HBM: experts are split into num_ranks contiguous
+ * blocks of num_experts/num_ranks, and rank r's rows are
+ * [recv_rank_offset[r], recv_rank_offset[r+1]).
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * Pointers.  Every array argument is a DEVICE pointer (HBM of the current HIP
+ * device), row-major and densely packed, owned by the caller; the library
+ * keeps no reference after the call returns and allocates nothing.  The
+ * workspace is caller-owned device memory of at least the size reported by
+ * the matching *_workspace_bytes() call; its contents on entry do not matter
+ * and on exit are unspecified.
+ *
+ * bf16 data is passed as raw 16-bit patterns (void*).
+ *
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Every call
+ * only validates its arguments on the host and enqueues kernels on `stream`;
+ * it never synchronises.  Outputs are valid once the stream reaches that
+ * point.  Calls on different streams touching disjoint buffers may run
+ * concurrently; the library holds no mutable global state.
+ *
+ * Routing slots.  Slot (t, j) is valid iff 0 <= topk_idx[t*k + j] <
+ * num_experts.  Any other value (conventionally -1) is an empty slot: it gets
+ * no receive row, no count, and token_row = -1.  The same expert may appear
+ * twice in a token; each slot then gets its own row.
+ *
+ * Receive order.  Rows are grouped by expert (ascending), so every rank's
+ * experts are one contiguous range; inside an expert, rows follow (t, j)
+ * ascending.  This order is unique, so every index output is deterministic
+ * and bit-reproducible.  Receive buffers are sized at capacity
+ * num_tokens * num_topk rows; the filled row count is
+ * recv_expert_offset[num_experts]; rows beyond it are not written.
+ *
+ * Errors.  Every entry point returns an ep_status_t (as int).  Invalid
+ * arguments are detected on the host before anything is enqueued and leave
+ * all outputs untouched.  EP_ERR_HIP reports a failed launch
+ * (hipGetLastError).  ep_last_error() returns a thread-local description of
+ * the last failure on the calling thread.  No C++ exception crosses the ABI.
+ */
+#ifndef EP_MI355X_EP_H
+#define EP_MI355X_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EP_OK = 0,
+    EP_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, misalignment, ... */
+    EP_ERR_UNSUPPORTED = 2,        /* valid but beyond this build's limits      */
+    EP_ERR_WORKSPACE_TOO_SMALL = 3,
+    EP_ERR_HIP = 4                 /* a HIP runtime call or launch failed        */
+} ep_status_t;
+
+/* Limits of this build (EP_ERR_UNSUPPORTED beyond them). */
+#define EP_MAX_TOPK 64          /* num_topk                                   */
+#define EP_MAX_RANKS 64         /* num_ranks                                  */
+#define EP_MAX_EXPERTS 2048     /* num_experts                                */
+
+/* Static description of a status code; never NULL. */
+const char* ep_status_string(int status);
+
+/* Thread-local text of the last non-EP_OK status returned on this thread. */
+const char* ep_last_error(void);
+
+/* Library version string, e.g. "ep-mi355x 0.1 gfx950". */
+const char* ep_version(void);
+
+/* ---------------------------------------------------------------------------
+ * ep_get_dispatch_layout -- routing histogram of one batch (get_dispatch_layout
+ * of the page's "Scope / Intranode"; the per-group count is the per-RDMA-rank
+ * count of "Scope / Internode HT", a group being ranks_per_group consecutive
+ * ranks).
+ *
+ *   topk_idx              [T, k] int64   routing (see "Routing slots")
+ *   num_tokens_per_rank   [R]    int32   out: tokens with >= 1 valid slot on r
+ *   num_tokens_per_group  [R/P]  int32   out: tokens touching any rank of group
+ *                                        g (may be NULL)
+ *   num_tokens_per_expert [E]    int32   out: valid slots routed to e
+ *   is_token_in_rank      [T, R] uint8   out: 1 iff token t has a valid slot on
+ *                                        rank r, else 0
+ *
+ * Requires T >= 0, 1 <= k <= EP_MAX_TOPK, 1 <= R <= EP_MAX_RANKS,
+ * E % R == 0, E <= EP_MAX_EXPERTS, 1 <= P, R % P == 0.  T == 0 writes zero
+ * counts.  Workspace: ep_layout_workspace_bytes(T, E, R, P).
+ * ------------------------------------------------------------------------- */
+size_t ep_layout_workspace_bytes(int64_t num_tokens, int num_experts, int num_ranks,
+                                 int ranks_per_group);
+
+int ep_get_dispatch_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
+                           int num_experts, int num_ranks, int ranks_per_group,
+                           int32_t* num_tokens_per_rank, int32_t* num_tokens_per_group,
+                           int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ep_dispatch -- permute each token's hidden vector into the contiguous
+ * per-rank / per-expert receive buffer (intranode dispatch of "Scope /
+ * Intranode"), and emit the receiver-side maps that combine consumes.
+ *
+ *   x                  [T, H]  bf16  in: token activations (16-byte aligned)
+ *   topk_idx           [T, k]  int64 in
+ *   topk_weights       [T, k]  fp32  in (may be NULL)
+ *   recv_x             [T*k, H] bf16 out: recv_x[token_row[t,j]] = x[t], bit
+ *                                    for bit (16-byte aligned)
+ *   recv_src_idx       [T*k]   int32 out: source token of each filled row
+ *   recv_topk_weights  [T*k]   fp32  out: topk_weights[t,j] of each filled row
+ *                                    (may be NULL; ignored if topk_weights is)
+ *   recv_expert_offset [E+1]   int32 out: first row of each expert; [E] = rows
+ *   recv_rank_offset   [R+1]   int32 out: recv_expert_offset[r*E/R] (may be NULL)
+ *   token_row          [T, k]  int32 out: row of slot (t,j), -1 if empty
+ *
+ * Requires H % 8 == 0 (rows are whole 16-byte vectors), T*k < 2^31, and the
+ * layout limits above.  Workspace: ep_dispatch_workspace_bytes(T, k, E).
+ * The offsets are computed from topk_idx itself, so no earlier call's output
+ * is trusted and every write stays inside the buffers described above.
+ * ------------------------------------------------------------------------- */
+size_t ep_dispatch_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts);
+
+int ep_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                int64_t num_tokens, int hidden, int num_topk, int num_experts, int num_ranks,
+                void* recv_x, int32_t* recv_src_idx, float* recv_topk_weights,
+                int32_t* recv_expert_offset, int32_t* recv_rank_offset, int32_t* token_row,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ep_dispatch_fp8 -- ep_dispatch with the low-latency FP8 cast (low-latency
+ * port commit, dispatch<kUseFP8,...>).  For token t and 128-channel block c:
+ *   a = max |x[t, 128c .. 128c+127]|,  s = a / 448 (IEEE fp32 division),
+ *   code = E4M3(x / s) (OCP E4M3FN, round to nearest even, saturating at
+ *   +-448), or 0x00 for every channel when s == 0.
+ * Every row of the token receives the same codes and scales:
+ *   recv_x_fp8  [T*k, H]     uint8 out: E4M3FN codes (16-byte aligned)
+ *   recv_scales [T*k, H/128] fp32  out: s per 128-channel block
+ * All other arguments as ep_dispatch.  Requires H % 128 == 0.
+ * Workspace: ep_dispatch_workspace_bytes(T, k, E).
+ * ------------------------------------------------------------------------- */
+int ep_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                    int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                    int num_ranks, uint8_t* recv_x_fp8, float* recv_scales,
+                    int32_t* recv_src_idx, float* recv_topk_weights,
+                    int32_t* recv_expert_offset, int32_t* recv_rank_offset,
+                    int32_t* token_row, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ep_combine -- gather each token's expert outputs back and sum them weighted
+ * by topk_weights (intranode combine of "Scope / Intranode", consuming the
+ * receiver-side map token_row that dispatch produced).  For every t, h:
+ *   acc = +0.0f;  for j = 0 .. k-1 in this order, if 0 <= token_row[t,j] < num_rows:
+ *       acc = fmaf(topk_weights[t,j], expert_out[token_row[t,j], h], acc);
+ *   combined_x[t, h] = bf16(acc), rounded to nearest even.
+ *
+ *   expert_out   [num_rows, H] bf16 in (16-byte aligned)
+ *   token_row    [T, k]        int32 in (from ep_dispatch; rows outside
+ *                              [0, num_rows) are skipped, never read)
+ *   topk_weights [T, k]        fp32  in
+ *   combined_x   [T, H]        bf16  out (16-byte aligned)
+ * Requires H % 8 == 0, 1 <= k <= EP_MAX_TOPK, num_rows >= 0.  No workspace.
+ * ------------------------------------------------------------------------- */
+int ep_combine(const void* expert_out, int64_t num_rows, const int32_t* token_row,
+               const float* topk_weights, int64_t num_tokens, int hidden, int num_topk,
+               void* combined_x, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_MI355X_EP_H */

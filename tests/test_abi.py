@@ -1,0 +1,118 @@
+"""CPU checks of the C ABI (no GPU needed, no kernel is ever launched here):
+libep.so loads, exports every function declared in include/ep.h, sizes its
+workspaces, and rejects invalid arguments on the host before enqueueing
+anything (every call below fails validation, so no HIP call is reached)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from combine_get_dispatch_02_amd import ep
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep.h")
+
+OK, EINVAL, EUNSUP, EWS = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x100000)        # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = ep.lib()
+    names = declared_functions()
+    assert {"ep_get_dispatch_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_combine"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"libep.so does not export {n}"
+
+
+def test_status_strings_and_version():
+    L = ep.lib()
+    assert L.ep_status_string(0) == b"EP_OK"
+    assert L.ep_status_string(3) == b"EP_ERR_WORKSPACE_TOO_SMALL"
+    assert L.ep_status_string(99) == b"EP_ERR_UNKNOWN"
+    assert b"gfx950" in L.ep_version()
+
+
+def test_workspace_sizes():
+    assert ep.ep_dispatch_workspace_bytes(4096, 8, 256) >= 16 * 256 * 4
+    assert ep.ep_dispatch_workspace_bytes(4096, 8, 256) % 256 == 0
+    assert ep.ep_layout_workspace_bytes(32768, 256, 32, 8) >= 128 * (256 + 32 + 4) * 4
+    assert ep.ep_dispatch_workspace_bytes(-1, 8, 256) == 0
+
+
+def _layout(**kw):
+    a = dict(idx=FAKE, T=16, k=2, E=8, R=4, P=2, per_rank=FAKE, per_group=None,
+             per_expert=FAKE, in_rank=FAKE, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return ep.lib().ep_get_dispatch_layout(a["idx"], a["T"], a["k"], a["E"], a["R"], a["P"],
+                                           a["per_rank"], a["per_group"], a["per_expert"],
+                                           a["in_rank"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), EINVAL), (dict(k=0), EINVAL), (dict(k=65), EUNSUP), (dict(E=6), EINVAL),
+    (dict(R=0), EINVAL), (dict(R=128, E=128), EUNSUP), (dict(E=4096, R=4), EUNSUP),
+    (dict(P=3), EINVAL), (dict(P=0), EINVAL), (dict(idx=None), EINVAL),
+    (dict(per_rank=None), EINVAL), (dict(in_rank=None), EINVAL), (dict(wsb=4), EWS),
+    (dict(ws=None), EWS), (dict(T=2 ** 28, k=8), EUNSUP),
+])
+def test_layout_rejects(kw, code):
+    assert _layout(**kw) == code
+    assert ep.lib().ep_last_error().startswith(b"ep_get_dispatch_layout")
+
+
+def _dispatch(fp8=False, **kw):
+    a = dict(x=FAKE, idx=FAKE, w=None, T=16, H=256, k=2, E=8, R=4, recv=FAKE, scales=FAKE,
+             src=FAKE, rw=None, eoff=FAKE, roff=None, trow=FAKE, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    L = ep.lib()
+    if fp8:
+        return L.ep_dispatch_fp8(a["x"], a["idx"], a["w"], a["T"], a["H"], a["k"], a["E"], a["R"],
+                                 a["recv"], a["scales"], a["src"], a["rw"], a["eoff"], a["roff"],
+                                 a["trow"], a["ws"], a["wsb"], None)
+    return L.ep_dispatch(a["x"], a["idx"], a["w"], a["T"], a["H"], a["k"], a["E"], a["R"],
+                         a["recv"], a["src"], a["rw"], a["eoff"], a["roff"], a["trow"], a["ws"],
+                         a["wsb"], None)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=12), EINVAL), (dict(H=0), EINVAL), (dict(x=None), EINVAL), (dict(recv=None), EINVAL),
+    (dict(src=None), EINVAL), (dict(trow=None), EINVAL), (dict(eoff=None), EINVAL),
+    (dict(x=ctypes.c_void_p(0x100008)), EINVAL), (dict(recv=ctypes.c_void_p(0x100004)), EINVAL),
+    (dict(wsb=16), EWS), (dict(ws=None), EWS), (dict(E=9), EINVAL), (dict(k=100), EUNSUP),
+])
+def test_dispatch_rejects(fp8, kw, code):
+    assert _dispatch(fp8=fp8, **kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(H=264), dict(scales=None), dict(scales=ctypes.c_void_p(0x100002))])
+def test_dispatch_fp8_specific_rejects(kw):
+    assert _dispatch(fp8=True, **kw) == EINVAL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), EINVAL), (dict(rows=-1), EINVAL), (dict(k=0), EINVAL), (dict(k=65), EUNSUP),
+    (dict(H=4), EINVAL), (dict(H=20), EINVAL), (dict(trow=None), EINVAL), (dict(w=None), EINVAL),
+    (dict(out=None), EINVAL), (dict(y=None), EINVAL), (dict(out=ctypes.c_void_p(0x100002)), EINVAL),
+    (dict(y=ctypes.c_void_p(0x100008)), EINVAL),
+])
+def test_combine_rejects(kw, code):
+    a = dict(y=FAKE, rows=32, trow=FAKE, w=FAKE, T=16, H=256, k=2, out=FAKE)
+    a.update(kw)
+    st = ep.lib().ep_combine(a["y"], a["rows"], a["trow"], a["w"], a["T"], a["H"], a["k"],
+                             a["out"], None)
+    assert st == code
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(ep, "_lib", None)
+    monkeypatch.setattr(ep, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        ep.lib()
