@@ -37,7 +37,10 @@ METRIC = "dispatch+combine effective GB/s and % of HBM peak at T=4096,H=7168,k=8
 HBM_PEAK_GBS = 8000.0
 FLUSH_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_dsv3_traffic.json")
-COMBINE_SRC = os.path.join(ROOT, "combine_get_dispatch_02_amd", "csrc", "combine.hip")
+# The combine kernel is defined by these two sources; counters taken on other
+# versions of them are not reported.
+COMBINE_SRCS = [os.path.join(ROOT, "combine_get_dispatch_02_amd", "csrc", f)
+                for f in ("combine.hip", "ep_device.h")]
 
 
 def log(msg):
@@ -58,9 +61,12 @@ def algorithmic_bytes(wl):
     )
 
 
-def sha_of(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def sources_sha256(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def load_traffic(per_launch_alg_bytes):
@@ -69,7 +75,7 @@ def load_traffic(per_launch_alg_bytes):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256") != sha_of(COMBINE_SRC):
+    if t.get("kernel_source_sha256") != sources_sha256(COMBINE_SRCS):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -137,6 +143,9 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between phases")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="after the timed steps, run 4 plain 256 MiB device copies (a known-size "
+                         "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -223,6 +232,14 @@ def main():
         step(i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    if args.calibration_copy:
+        cal_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        cal_dst = torch.empty_like(cal_src)
+        torch.cuda.synchronize()
+        for _ in range(4):
+            cal_dst.copy_(cal_src)
+        torch.cuda.synchronize()
 
     ms = {p: np.array([e[a].elapsed_time(e[b]) for e in evs])
           for p, (a, b) in zip(phases, [(0, 1), (1, 2), (3, 4), (5, 6)])}
