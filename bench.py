@@ -4,10 +4,12 @@
 One step is one pass of the whole hot path over one batch of synthetic
 input already resident in HBM:
     ep_get_dispatch_layout -> ep_dispatch -> ep_combine -> ep_dispatch_fp8
-with the combine fed the dispatched rows (identity experts).  A 512 MiB
-write between phases evicts L2 and the Infinity Cache, standing in for the
-expert computation that sits between dispatch and combine in a real model;
-it is outside every timed phase.
+with the combine fed the dispatched rows (identity experts).  Before each
+phase (outside its events) a 512 MiB write followed by a 512 MiB read of
+another buffer evicts L2 and the 256 MB Infinity Cache: the phase's inputs
+are then only in HBM and the caches hold clean, unrelated lines, so no
+write-back of earlier data lands inside a timed phase.  This stands in for
+the expert computation that separates dispatch from combine in a model.
 
 Each phase is bracketed by HIP events recorded on the stream the kernels are
 launched on (torch's current stream, which the binding passes to the C ABI).
@@ -35,7 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "dispatch+combine effective GB/s and % of HBM peak at T=4096,H=7168,k=8"
 HBM_PEAK_GBS = 8000.0
-FLUSH_BYTES = 512 << 20
+FLUSH_BYTES = 512 << 20           # written, then as much again read
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_dsv3_traffic.json")
 # The combine kernel is defined by these two sources; counters taken on other
 # versions of them are not reported.
@@ -193,12 +195,14 @@ def main():
     ws_d = torch.empty(ep.ep_dispatch_workspace_bytes(T, k, E), dtype=torch.uint8, device=dev)
     comb = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush_src = torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
 
     phases = ["layout", "dispatch", "combine", "dispatch_fp8"]
 
     def flush(i):
         if not args.no_flush:
             flush_buf.fill_(i & 0xFF)
+            flush_src.sum()
 
     def step(i, ev):
         flush(i)

@@ -10,13 +10,16 @@
 // and, inside an expert, ordered by (token, slot).
 //
 // Kernels (all deterministic; no global atomics):
-//   chunk_hist   per 256-token chunk, per-expert slot counts (LDS atomics)
-//   rows         per chunk: per-expert prefix over earlier chunks + block
-//                scan over experts -> chunk base rows; then the stable rank of
-//                every slot inside the chunk from wave64 ballot matching;
-//                writes token_row, recv_src_idx, recv_topk_weights, offsets
-//   copy_bf16    one wave per (token, column tile): 16-byte loads of x[t]
-//                once, 16-byte non-temporal stores into each of its k rows
+//   tile_hist    per tile of >= 64 tokens (at most 64 tiles at the benchmark
+//                sizes), per-expert slot counts (LDS atomics)
+//   rows         per tile: per-expert prefix over earlier tiles + block scan
+//                over experts -> tile base rows; each lane holds its slots'
+//                ids in registers; the stable rank of every slot inside the tile from wave64
+//                ballot matching; writes token_row, recv_src_idx,
+//                recv_topk_weights and the offsets
+//   copy_bf16    one block per (token, 2 KB column segment), one wave per
+//                destination row: x[t] shared through L2, two 16-byte
+//                non-temporal stores per lane per row
 //   copy_fp8     same walk; per 128-channel block amax over 8 lanes, scale
 //                amax/448, E4M3FN codes, 16-byte code stores + scale stores
 #include "ep_device.h"
@@ -26,16 +29,22 @@ namespace ep {
 namespace {
 
 constexpr int kIndexWaves = kIndexThreads / kWave;
+constexpr int kHistBatch = 64;
 
-__global__ __launch_bounds__(kIndexThreads) void chunk_hist_kernel(
-    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int32_t* __restrict__ hist) {
+// Per-tile expert histogram: hist[tile][e] = valid slots of the tile's tokens
+// routed to e (LDS atomics; integer sums do not depend on order).
+__global__ __launch_bounds__(kIndexThreads) void tile_hist_kernel(
+    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int tile_tokens,
+    int32_t* __restrict__ hist) {
     extern __shared__ int32_t h[];
     for (int e = threadIdx.x; e < E; e += kIndexThreads) h[e] = 0;
     __syncthreads();
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kChunkTokens;
-    const int64_t t1 = t0 + kChunkTokens < T ? t0 + kChunkTokens : T;
-    for (int64_t s = t0 * k + threadIdx.x; s < t1 * k; s += kIndexThreads) {
-        const int64_t e = topk_idx[s];
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tile_tokens;
+    const int nt = static_cast<int>(T - t0 < tile_tokens ? T - t0 : tile_tokens);
+    const int S = nt * k;
+    const int64_t* ids = topk_idx + t0 * k;
+    for (int s = threadIdx.x; s < S; s += kIndexThreads) {
+        const int64_t e = ids[s];
         if (e >= 0 && e < E) atomicAdd(&h[e], 1);
     }
     __syncthreads();
@@ -78,32 +87,67 @@ __device__ int block_exclusive_scan(int32_t* a, int n, int32_t* wave_tot) {
     return total;
 }
 
+// One block per tile.  Wave w owns the tile's slots [w*Q, (w+1)*Q) (Q a
+// multiple of 64) and lane l of it the slots w*Q + 64*i + l, whose ids and
+// weights it holds in registers (at most kSlotsPerLane of them).
+// LDS: base[E] (first row of each expert in this tile), wc[kIndexWaves][E]
+// (per-wave cursors), wave_tot[kIndexWaves].
+constexpr int kSlotsPerLane = kMaxTileSlots / kIndexThreads;
+
 __global__ __launch_bounds__(kIndexThreads) void rows_kernel(
     const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int64_t T,
-    int k, int E, int R, int nchunks, int nbits, const int32_t* __restrict__ hist,
+    int k, int E, int R, int tile_tokens, int ntiles, int nbits, const int32_t* __restrict__ hist,
     int32_t* __restrict__ token_row, int32_t* __restrict__ recv_src_idx,
     float* __restrict__ recv_w, int32_t* __restrict__ expert_offset,
     int32_t* __restrict__ rank_offset) {
     extern __shared__ int32_t lds[];
-    int32_t* base = lds;                          // [E]  first row of (chunk, expert)
-    int32_t* wc = lds + E;                        // [kIndexWaves][E] per-wave cursors
+    int32_t* base = lds;
+    int32_t* wc = lds + E;
     int32_t* wave_tot = lds + (1 + kIndexWaves) * E;
     const int c = blockIdx.x;
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
+    const int64_t t0 = static_cast<int64_t>(c) * tile_tokens;
+    const int nt = static_cast<int>(T - t0 < tile_tokens ? T - t0 : tile_tokens);
+    const int S = nt * k;
+    const int64_t s0 = t0 * k;
+    const int Q = (S + kIndexThreads - 1) / kIndexThreads * kWave;
 
-    // 1. Per expert: slots in all chunks (-> base, scanned below) and in the
-    //    chunks before this one (-> wc[0], added after the scan).
+    // 0. This lane's slots: raw ids and weights, loads issued first so that
+    //    their latency overlaps the histogram loads below.
+    int64_t raw[kSlotsPerLane];
+    float wt[kSlotsPerLane];
+#pragma unroll
+    for (int i = 0; i < kSlotsPerLane; ++i) {
+        const int s = wave * Q + i * kWave + lane;
+        const bool in = i * kWave < Q && s < S;
+        raw[i] = in ? topk_idx[s0 + s] : -1;
+        wt[i] = (in && recv_w) ? topk_weights[s0 + s] : 0.0f;
+    }
+    // 1. Per expert: valid slots in all tiles (scanned below into the expert
+    //    offsets) and in the tiles before this one.  The histograms were
+    //    written by blocks on every XCD, so most of them come from beyond this
+    //    XCD's L2: issue them kHistBatch at a time so their latencies overlap.
     for (int e = threadIdx.x; e < E; e += kIndexThreads) {
         int tot = 0, pre = 0;
-        for (int cc = 0; cc < nchunks; ++cc) {
-            const int v = hist[static_cast<int64_t>(cc) * E + e];
-            tot += v;
-            pre += (cc < c) ? v : 0;
+        for (int c0 = 0; c0 < ntiles; c0 += kHistBatch) {
+            int v[kHistBatch];
+#pragma unroll
+            for (int i = 0; i < kHistBatch; ++i)
+                v[i] = (c0 + i < ntiles) ? hist[static_cast<int64_t>(c0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < kHistBatch; ++i) {
+                tot += v[i];
+                pre += (c0 + i < c) ? v[i] : 0;
+            }
         }
         base[e] = tot;
         wc[e] = pre;
     }
+    int ids[kSlotsPerLane];
+#pragma unroll
+    for (int i = 0; i < kSlotsPerLane; ++i)
+        ids[i] = (raw[i] >= 0 && raw[i] < E) ? static_cast<int>(raw[i]) : -1;
     __syncthreads();
     const int total = block_exclusive_scan(base, E, wave_tot);
     if (c == 0) {
@@ -115,24 +159,15 @@ __global__ __launch_bounds__(kIndexThreads) void rows_kernel(
     }
     for (int e = threadIdx.x; e < E; e += kIndexThreads) base[e] += wc[e];
     __syncthreads();
-
-    // 2. Slots of this chunk, split into kIndexWaves contiguous ranges of Q
-    //    (a multiple of 64) slots; each wave counts its range per expert.
-    const int64_t t0 = static_cast<int64_t>(c) * kChunkTokens;
-    const int64_t s0 = t0 * k;
-    const int nt = static_cast<int>(T - t0 < kChunkTokens ? T - t0 : kChunkTokens);
-    const int S = nt * k;
-    const int Q = (S + kIndexThreads - 1) / kIndexThreads * kWave;
     for (int i = threadIdx.x; i < kIndexWaves * E; i += kIndexThreads) wc[i] = 0;
     __syncthreads();
+
+    // 2. Each wave counts its range per expert; the waves' cursors are then
+    //    seeded in wave order.
     int32_t* my = wc + wave * E;
-    for (int i = lane; i < Q; i += kWave) {
-        const int s = wave * Q + i;
-        if (s < S) {
-            const int64_t e = topk_idx[s0 + s];
-            if (e >= 0 && e < E) atomicAdd(&my[e], 1);
-        }
-    }
+#pragma unroll
+    for (int i = 0; i < kSlotsPerLane; ++i)
+        if (ids[i] >= 0) atomicAdd(&my[ids[i]], 1);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kIndexThreads) {
         int run = base[e];
@@ -148,13 +183,14 @@ __global__ __launch_bounds__(kIndexThreads) void rows_kernel(
     //    row = its wave's cursor for the expert + number of lower lanes with
     //    the same expert; the highest such lane then advances the cursor.
     //    (LDS accesses of one wave complete in program order.)
-    for (int g = 0; g < Q; g += kWave) {
-        const int s = wave * Q + g + lane;
+#pragma unroll
+    for (int i = 0; i < kSlotsPerLane; ++i) {
+        if (i * kWave >= Q) break;
+        const int s = wave * Q + i * kWave + lane;
         const bool in = s < S;
-        const int64_t e64 = in ? topk_idx[s0 + s] : -1;
-        const bool valid = in && e64 >= 0 && e64 < E;
-        const int e = valid ? static_cast<int>(e64) : 0;
-        const uint64_t peers = match_key(e, valid, nbits);
+        const int e = ids[i];
+        const bool valid = e >= 0;
+        const uint64_t peers = match_key(valid ? e : 0, valid, nbits);
         int row = -1;
         if (valid) row = my[e] + __popcll(peers & lanes_below());
         if (valid && (peers >> lane) == 1) my[e] += __popcll(peers);
@@ -162,8 +198,9 @@ __global__ __launch_bounds__(kIndexThreads) void rows_kernel(
             const int64_t gs = s0 + s;
             token_row[gs] = row;
             if (valid) {
-                recv_src_idx[row] = static_cast<int32_t>(gs / k);
-                if (recv_w) recv_w[row] = topk_weights[gs];
+                recv_src_idx[row] = static_cast<int32_t>(t0) +
+                                    static_cast<int32_t>(static_cast<unsigned>(s) / static_cast<unsigned>(k));
+                if (recv_w) recv_w[row] = wt[i];
             }
         }
     }
@@ -181,34 +218,39 @@ __device__ __forceinline__ int64_t wave_index() {
            __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
 }
 
-// bf16 copy: tile = (token t, U*64 consecutive 16-byte vectors of its row).
-template <int U>
-__global__ __launch_bounds__(256) void copy_bf16_kernel(const u32x4* __restrict__ x,
+// bf16 copy: one block per (token t, column segment of kCopyVec*64 16-byte
+// vectors = 2 KB), one wave per destination row.  The block has
+// kb = min(k, 8) waves; wave w writes rows j = w, w + kb, ... of the token.
+// Every wave loads the same segment of x[t] with plain (cached) loads, so the
+// kb waves of the block (same CU, same XCD) share it through L2 and HBM reads
+// it once; each lane then issues kCopyVec 16-byte non-temporal stores per
+// row.  On MI355X this drains a 1:k fan-out faster than one wave storing one
+// load to all k rows (measured: ~6% at 4096 x 7168, k = 8); longer runs per
+// wave (4 or 7 vectors per lane) were markedly slower.
+constexpr int kCopyVec = 2;
+
+__global__ __launch_bounds__(512) void copy_bf16_kernel(const u32x4* __restrict__ x,
                                                         const int32_t* __restrict__ token_row,
                                                         u32x4* __restrict__ recv, int V, int k,
-                                                        int tiles_per_token, int64_t num_tiles) {
+                                                        int kb, int segs) {
     const int lane = lane_id();
-    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (blockDim.x / kWave);
-    for (int64_t tile = wave_index(); tile < num_tiles; tile += nwaves) {
-        const int64_t t = tile / tiles_per_token;
-        const int v0 = static_cast<int>(tile - t * tiles_per_token) * (U * kWave) + lane;
-        const u32x4* src = x + t * V;
-        u32x4 val[U];
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int64_t t = blockIdx.x / segs;
+    const int v0 = static_cast<int>(blockIdx.x - t * segs) * (kCopyVec * kWave) + lane;
+    u32x4 val[kCopyVec];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < kCopyVec; ++u) {
+        const int v = v0 + u * kWave;
+        if (v < V) val[u] = x[t * V + v];
+    }
+    for (int j = w; j < k; j += kb) {
+        const int r = token_row[t * k + j];
+        if (r < 0) continue;
+        u32x4* dst = recv + static_cast<int64_t>(r) * V;
+#pragma unroll
+        for (int u = 0; u < kCopyVec; ++u) {
             const int v = v0 + u * kWave;
-            if (v < V) val[u] = __builtin_nontemporal_load(src + v);
-        }
-        const int my_row = lane < k ? token_row[t * k + lane] : -1;
-        for (int j = 0; j < k; ++j) {
-            const int r = read_lane(my_row, j);
-            if (r < 0) continue;
-            u32x4* dst = recv + static_cast<int64_t>(r) * V;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int v = v0 + u * kWave;
-                if (v < V) __builtin_nontemporal_store(val[u], dst + v);
-            }
+            if (v < V) __builtin_nontemporal_store(val[u], dst + v);
         }
     }
 }
@@ -268,24 +310,23 @@ __global__ __launch_bounds__(256) void copy_fp8_kernel(const u32x4* __restrict__
     }
 }
 
-template <int U>
-hipError_t launch_copy_bf16_u(const void* x, const int32_t* token_row, void* recv, int64_t T,
-                              int V, int k, hipStream_t stream) {
-    const int tiles_per_token = static_cast<int>(ceil_div(V, U * kWave));
-    const int64_t num_tiles = T * tiles_per_token;
-    const int64_t blocks = ceil_div(num_tiles, 4);
-    const unsigned grid = static_cast<unsigned>(blocks < (1 << 30) ? blocks : (1 << 30));
-    hipLaunchKernelGGL(copy_bf16_kernel<U>, dim3(grid), dim3(256), 0, stream,
-                       static_cast<const u32x4*>(x), token_row, static_cast<u32x4*>(recv), V, k,
-                       tiles_per_token, num_tiles);
-    return hipGetLastError();
-}
-
 }  // namespace
 
-size_t index_workspace_bytes(int64_t T, int E) {
-    const int64_t nchunks = ceil_div(T, kChunkTokens);
-    const size_t b = static_cast<size_t>(nchunks) * static_cast<size_t>(E) * sizeof(int32_t);
+// Tokens per tile of the receive-order kernels: a multiple of 64, at least 64,
+// large enough that there are at most kMaxTiles tiles (each tile sums the
+// histograms of the tiles before it), and small enough that a tile's ids fit
+// the kMaxTileSlots LDS budget.
+static int index_tile_tokens(int64_t T, int k) {
+    int64_t tt = ceil_div(T, kMaxTiles);
+    tt = ceil_div(tt < 64 ? 64 : tt, 64) * 64;
+    int64_t cap = (kMaxTileSlots / k) / 64 * 64;
+    if (cap < 64) cap = 64;
+    return static_cast<int>(tt < cap ? tt : cap);
+}
+
+size_t index_workspace_bytes(int64_t T, int k, int E) {
+    const int64_t ntiles = T > 0 ? ceil_div(T, index_tile_tokens(T, k)) : 0;
+    const size_t b = static_cast<size_t>(ntiles) * static_cast<size_t>(E) * sizeof(int32_t);
     return round_up(b > 0 ? b : 1, 256);
 }
 
@@ -298,14 +339,15 @@ hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weig
                            rank_offset, R);
         return hipGetLastError();
     }
-    const int nchunks = static_cast<int>(ceil_div(T, kChunkTokens));
+    const int tt = index_tile_tokens(T, k);
+    const int ntiles = static_cast<int>(ceil_div(T, tt));
     int32_t* hist = static_cast<int32_t*>(workspace);
-    hipLaunchKernelGGL(chunk_hist_kernel, dim3(nchunks), dim3(kIndexThreads),
-                       static_cast<size_t>(E) * sizeof(int32_t), stream, topk_idx, T, k, E, hist);
+    hipLaunchKernelGGL(tile_hist_kernel, dim3(ntiles), dim3(kIndexThreads),
+                       static_cast<size_t>(E) * sizeof(int32_t), stream, topk_idx, T, k, E, tt, hist);
     const int nbits = E > 1 ? 32 - __builtin_clz(static_cast<unsigned>(E - 1)) : 0;
     const size_t lds = (static_cast<size_t>(1 + kIndexWaves) * E + kIndexWaves) * sizeof(int32_t);
-    hipLaunchKernelGGL(rows_kernel, dim3(nchunks), dim3(kIndexThreads), lds, stream, topk_idx,
-                       (recv_w ? topk_weights : nullptr), T, k, E, R, nchunks, nbits, hist,
+    hipLaunchKernelGGL(rows_kernel, dim3(ntiles), dim3(kIndexThreads), lds, stream, topk_idx,
+                       (recv_w ? topk_weights : nullptr), T, k, E, R, tt, ntiles, nbits, hist,
                        token_row, recv_src_idx, (topk_weights ? recv_w : nullptr), expert_offset,
                        rank_offset);
     return hipGetLastError();
@@ -315,18 +357,12 @@ hipError_t launch_dispatch_copy_bf16(const void* x, const int32_t* token_row, vo
                                      int64_t T, int H, int k, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
-    // Largest tile (more bytes in flight per wave) that divides the row and
-    // still leaves enough waves to fill 256 CUs.
-    const int64_t want_waves = 4096;
-    if (V % (8 * kWave) == 0 && T * (V / (8 * kWave)) >= want_waves)
-        return launch_copy_bf16_u<8>(x, token_row, recv_x, T, V, k, stream);
-    if (V % (7 * kWave) == 0 && T * (V / (7 * kWave)) >= want_waves)
-        return launch_copy_bf16_u<7>(x, token_row, recv_x, T, V, k, stream);
-    if (V % (4 * kWave) == 0 && T * (V / (4 * kWave)) >= want_waves)
-        return launch_copy_bf16_u<4>(x, token_row, recv_x, T, V, k, stream);
-    if (V % (2 * kWave) == 0 && T * (V / (2 * kWave)) >= want_waves)
-        return launch_copy_bf16_u<2>(x, token_row, recv_x, T, V, k, stream);
-    return launch_copy_bf16_u<1>(x, token_row, recv_x, T, V, k, stream);
+    const int segs = static_cast<int>(ceil_div(V, kCopyVec * kWave));
+    const int kb = k < 8 ? k : 8;
+    hipLaunchKernelGGL(copy_bf16_kernel, dim3(static_cast<unsigned>(T * segs)), dim3(kb * kWave), 0,
+                       stream, static_cast<const u32x4*>(x), token_row, static_cast<u32x4*>(recv_x), V,
+                       k, kb, segs);
+    return hipGetLastError();
 }
 
 hipError_t launch_dispatch_copy_fp8(const void* x, const int32_t* token_row, uint8_t* recv_q,

@@ -56,9 +56,9 @@ int check_dispatch_common(const char* fn, const void* x, const int64_t* topk_idx
         return fail(EP_ERR_INVALID_ARGUMENT, "%s: a required pointer is NULL", fn);
     if (T > 0 && (!aligned16(x) || !aligned16(recv)))
         return fail(EP_ERR_INVALID_ARGUMENT, "%s: x and the receive buffer must be 16-byte aligned", fn);
-    if (T > 0 && ws_bytes < ep::index_workspace_bytes(T, E))
+    if (T > 0 && ws_bytes < ep::index_workspace_bytes(T, k, E))
         return fail(EP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes", fn,
-                    ep::index_workspace_bytes(T, E));
+                    ep::index_workspace_bytes(T, k, E));
     return EP_OK;
 }
 
@@ -114,7 +114,7 @@ int ep_get_dispatch_layout(const int64_t* topk_idx, int64_t num_tokens, int num_
 
 size_t ep_dispatch_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts) {
     if (num_tokens < 0 || num_topk < 1 || num_experts < 1) return 0;
-    return ep::index_workspace_bytes(num_tokens, num_experts);
+    return ep::index_workspace_bytes(num_tokens, num_topk, num_experts);
 }
 
 int ep_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weights,

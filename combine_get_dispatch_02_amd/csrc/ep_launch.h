@@ -12,9 +12,11 @@ namespace ep {
 
 // Tokens per block of the layout histogram kernel (one token per thread).
 constexpr int kLayoutTokensPerBlock = 256;
-// Tokens per chunk of the receive-order computation.  Rows are ranked inside
-// a chunk with wave ballots; chunks are chained by per-expert prefix sums.
-constexpr int kChunkTokens = 256;
+// Receive-order computation: tokens are cut into tiles (at most kMaxTiles of
+// them while a tile's slots fit kMaxTileSlots); rows are ranked inside a tile
+// with wave ballots, and tiles are chained by per-expert prefix sums.
+constexpr int kMaxTiles = 64;
+constexpr int kMaxTileSlots = 4096;
 constexpr int kIndexThreads = 256;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -27,7 +29,7 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R
                          uint8_t* in_rank, void* workspace, hipStream_t stream);
 
 // ---- receive order (shared by both dispatch variants) -------------------------
-size_t index_workspace_bytes(int64_t T, int E);
+size_t index_workspace_bytes(int64_t T, int k, int E);
 hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weights, int64_t T,
                                  int k, int E, int R, int32_t* recv_src_idx, float* recv_w,
                                  int32_t* expert_offset, int32_t* rank_offset,
