@@ -30,6 +30,10 @@ namespace {
 
 constexpr int kIndexWaves = kIndexThreads / kWave;
 constexpr int kHistBatch = 64;
+constexpr int kSlotsPerLane = kMaxTileSlots / kIndexThreads;
+// Fused receive-order kernel: every block histograms all T*k slots itself.
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedBatch = 32;   // slots per thread per sweep step (loads in flight)
 
 // Per-tile expert histogram: hist[tile][e] = valid slots of the tile's tokens
 // routed to e (LDS atomics; integer sums do not depend on order).
@@ -52,10 +56,12 @@ __global__ __launch_bounds__(kIndexThreads) void tile_hist_kernel(
     for (int e = threadIdx.x; e < E; e += kIndexThreads) out[e] = h[e];
 }
 
-// In-place exclusive scan of a[0..n) held in LDS, n <= 8 * kIndexThreads.
-// Every thread gets the total.  Caller synchronises before; this syncs after.
+// In-place exclusive scan of a[0..n) held in LDS by a block of NT threads,
+// n <= 8 * NT.  Every thread gets the total.  Caller synchronises before;
+// this syncs after.
+template <int NT>
 __device__ int block_exclusive_scan(int32_t* a, int n, int32_t* wave_tot) {
-    const int ipt = (n + kIndexThreads - 1) / kIndexThreads;
+    const int ipt = (n + NT - 1) / NT;
     const int b = threadIdx.x * ipt;
     int sum = 0;
     for (int i = 0; i < ipt; ++i)
@@ -72,7 +78,7 @@ __device__ int block_exclusive_scan(int32_t* a, int n, int32_t* wave_tot) {
     __syncthreads();
     int base = 0, total = 0;
 #pragma unroll
-    for (int w = 0; w < kIndexWaves; ++w) {
+    for (int w = 0; w < NT / kWave; ++w) {
         base += (w < wave) ? wave_tot[w] : 0;
         total += wave_tot[w];
     }
@@ -87,89 +93,52 @@ __device__ int block_exclusive_scan(int32_t* a, int n, int32_t* wave_tot) {
     return total;
 }
 
-// One block per tile.  Wave w owns the tile's slots [w*Q, (w+1)*Q) (Q a
-// multiple of 64) and lane l of it the slots w*Q + 64*i + l, whose ids and
-// weights it holds in registers (at most kSlotsPerLane of them).
-// LDS: base[E] (first row of each expert in this tile), wc[kIndexWaves][E]
-// (per-wave cursors), wave_tot[kIndexWaves].
-constexpr int kSlotsPerLane = kMaxTileSlots / kIndexThreads;
-
-__global__ __launch_bounds__(kIndexThreads) void rows_kernel(
-    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int64_t T,
-    int k, int E, int R, int tile_tokens, int ntiles, int nbits, const int32_t* __restrict__ hist,
-    int32_t* __restrict__ token_row, int32_t* __restrict__ recv_src_idx,
-    float* __restrict__ recv_w, int32_t* __restrict__ expert_offset,
-    int32_t* __restrict__ rank_offset) {
-    extern __shared__ int32_t lds[];
-    int32_t* base = lds;
-    int32_t* wc = lds + E;
-    int32_t* wave_tot = lds + (1 + kIndexWaves) * E;
-    const int c = blockIdx.x;
+// The tile's slots are ranked by the block's first kIndexWaves waves: wave w
+// owns slots [w*Q, (w+1)*Q) (Q a multiple of 64), lane l of it the slots
+// w*Q + 64*i + l, whose raw ids and weights it loads into registers here.
+__device__ __forceinline__ void load_tile_slots(const int64_t* __restrict__ topk_idx,
+                                                const float* __restrict__ topk_weights,
+                                                bool want_w, int64_t s0, int S, int Q,
+                                                int64_t (&raw)[kSlotsPerLane],
+                                                float (&wt)[kSlotsPerLane]) {
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
-    const int64_t t0 = static_cast<int64_t>(c) * tile_tokens;
-    const int nt = static_cast<int>(T - t0 < tile_tokens ? T - t0 : tile_tokens);
-    const int S = nt * k;
-    const int64_t s0 = t0 * k;
-    const int Q = (S + kIndexThreads - 1) / kIndexThreads * kWave;
-
-    // 0. This lane's slots: raw ids and weights, loads issued first so that
-    //    their latency overlaps the histogram loads below.
-    int64_t raw[kSlotsPerLane];
-    float wt[kSlotsPerLane];
+    const bool ranker = threadIdx.x < kIndexThreads;
 #pragma unroll
     for (int i = 0; i < kSlotsPerLane; ++i) {
         const int s = wave * Q + i * kWave + lane;
-        const bool in = i * kWave < Q && s < S;
+        const bool in = ranker && i * kWave < Q && s < S;
         raw[i] = in ? topk_idx[s0 + s] : -1;
-        wt[i] = (in && recv_w) ? topk_weights[s0 + s] : 0.0f;
+        wt[i] = (in && want_w) ? topk_weights[s0 + s] : 0.0f;
     }
-    // 1. Per expert: valid slots in all tiles (scanned below into the expert
-    //    offsets) and in the tiles before this one.  The histograms were
-    //    written by blocks on every XCD, so most of them come from beyond this
-    //    XCD's L2: issue them kHistBatch at a time so their latencies overlap.
-    for (int e = threadIdx.x; e < E; e += kIndexThreads) {
-        int tot = 0, pre = 0;
-        for (int c0 = 0; c0 < ntiles; c0 += kHistBatch) {
-            int v[kHistBatch];
-#pragma unroll
-            for (int i = 0; i < kHistBatch; ++i)
-                v[i] = (c0 + i < ntiles) ? hist[static_cast<int64_t>(c0 + i) * E + e] : 0;
-#pragma unroll
-            for (int i = 0; i < kHistBatch; ++i) {
-                tot += v[i];
-                pre += (c0 + i < c) ? v[i] : 0;
-            }
-        }
-        base[e] = tot;
-        wc[e] = pre;
-    }
-    int ids[kSlotsPerLane];
-#pragma unroll
-    for (int i = 0; i < kSlotsPerLane; ++i)
-        ids[i] = (raw[i] >= 0 && raw[i] < E) ? static_cast<int>(raw[i]) : -1;
-    __syncthreads();
-    const int total = block_exclusive_scan(base, E, wave_tot);
-    if (c == 0) {
-        const int epr = E / R;
-        for (int e = threadIdx.x; e <= E; e += kIndexThreads) expert_offset[e] = e < E ? base[e] : total;
-        if (rank_offset)
-            for (int r = threadIdx.x; r <= R; r += kIndexThreads)
-                rank_offset[r] = r < R ? base[r * epr] : total;
-    }
-    for (int e = threadIdx.x; e < E; e += kIndexThreads) base[e] += wc[e];
-    __syncthreads();
-    for (int i = threadIdx.x; i < kIndexWaves * E; i += kIndexThreads) wc[i] = 0;
-    __syncthreads();
+}
 
-    // 2. Each wave counts its range per expert; the waves' cursors are then
-    //    seeded in wave order.
-    int32_t* my = wc + wave * E;
-#pragma unroll
-    for (int i = 0; i < kSlotsPerLane; ++i)
-        if (ids[i] >= 0) atomicAdd(&my[ids[i]], 1);
+// Shared tail of both receive-order paths.  base[e] (LDS) holds the first row
+// of expert e for this tile.  Each ranking wave counts its range per expert,
+// the waves' cursors are seeded in wave order, then each wave walks its range
+// 64 slots at a time, in order: a slot's row = its wave's cursor for the
+// expert + the number of lower lanes with the same expert (wave64 ballot
+// matching); the highest such lane then advances the cursor (LDS accesses of
+// one wave complete in program order).  Called by every thread of the block.
+__device__ __forceinline__ void rank_tile(const int (&ids)[kSlotsPerLane],
+                                          const float (&wt)[kSlotsPerLane], const int32_t* base,
+                                          int32_t* wc, int E, int S, int Q, int64_t s0, int64_t t0,
+                                          int k, int nbits, int32_t* __restrict__ token_row,
+                                          int32_t* __restrict__ recv_src_idx,
+                                          float* __restrict__ recv_w) {
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const bool ranker = threadIdx.x < kIndexThreads;
+    for (int i = threadIdx.x; i < kIndexWaves * E; i += blockDim.x) wc[i] = 0;
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += kIndexThreads) {
+    int32_t* my = wc + (ranker ? wave : 0) * E;
+    if (ranker) {
+#pragma unroll
+        for (int i = 0; i < kSlotsPerLane; ++i)
+            if (ids[i] >= 0) atomicAdd(&my[ids[i]], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
         int run = base[e];
         for (int w = 0; w < kIndexWaves; ++w) {
             const int v = wc[w * E + e];
@@ -178,11 +147,7 @@ __global__ __launch_bounds__(kIndexThreads) void rows_kernel(
         }
     }
     __syncthreads();
-
-    // 3. Each wave walks its range 64 slots at a time, in order.  A slot's
-    //    row = its wave's cursor for the expert + number of lower lanes with
-    //    the same expert; the highest such lane then advances the cursor.
-    //    (LDS accesses of one wave complete in program order.)
+    if (!ranker) return;
 #pragma unroll
     for (int i = 0; i < kSlotsPerLane; ++i) {
         if (i * kWave >= Q) break;
@@ -204,6 +169,166 @@ __global__ __launch_bounds__(kIndexThreads) void rows_kernel(
             }
         }
     }
+}
+
+__device__ __forceinline__ void write_offsets(const int32_t* eoff, int total, int E, int R,
+                                              int32_t* __restrict__ expert_offset,
+                                              int32_t* __restrict__ rank_offset) {
+    const int epr = E / R;
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) expert_offset[e] = e < E ? eoff[e] : total;
+    if (rank_offset)
+        for (int r = threadIdx.x; r <= R; r += blockDim.x) rank_offset[r] = r < R ? eoff[r * epr] : total;
+}
+
+// Two-kernel path, second kernel: one block per tile.  Per expert, the tile
+// histograms of all tiles (-> expert offsets) and of the tiles before this
+// one (-> this tile's base rows).  LDS: base[E], wc[kIndexWaves][E],
+// wave_tot[kIndexWaves].
+__global__ __launch_bounds__(kIndexThreads) void rows_kernel(
+    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int64_t T,
+    int k, int E, int R, int tile_tokens, int ntiles, int nbits, const int32_t* __restrict__ hist,
+    int32_t* __restrict__ token_row, int32_t* __restrict__ recv_src_idx,
+    float* __restrict__ recv_w, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ rank_offset) {
+    extern __shared__ int32_t lds[];
+    int32_t* base = lds;
+    int32_t* wc = lds + E;
+    int32_t* wave_tot = lds + (1 + kIndexWaves) * E;
+    const int c = blockIdx.x;
+    const int64_t t0 = static_cast<int64_t>(c) * tile_tokens;
+    const int nt = static_cast<int>(T - t0 < tile_tokens ? T - t0 : tile_tokens);
+    const int S = nt * k;
+    const int64_t s0 = t0 * k;
+    const int Q = (S + kIndexThreads - 1) / kIndexThreads * kWave;
+
+    int64_t raw[kSlotsPerLane];
+    float wt[kSlotsPerLane];
+    load_tile_slots(topk_idx, topk_weights, recv_w != nullptr, s0, S, Q, raw, wt);
+    // The histograms were written by blocks on every XCD, so most come from
+    // beyond this XCD's L2: issue them kHistBatch at a time.
+    for (int e = threadIdx.x; e < E; e += kIndexThreads) {
+        int tot = 0, pre = 0;
+        for (int c0 = 0; c0 < ntiles; c0 += kHistBatch) {
+            int v[kHistBatch];
+#pragma unroll
+            for (int i = 0; i < kHistBatch; ++i)
+                v[i] = (c0 + i < ntiles) ? hist[static_cast<int64_t>(c0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < kHistBatch; ++i) {
+                tot += v[i];
+                pre += (c0 + i < c) ? v[i] : 0;
+            }
+        }
+        base[e] = tot;
+        wc[e] = pre;
+    }
+    int ids[kSlotsPerLane];
+#pragma unroll
+    for (int i = 0; i < kSlotsPerLane; ++i)
+        ids[i] = (raw[i] >= 0 && raw[i] < E) ? static_cast<int>(raw[i]) : -1;
+    __syncthreads();
+    const int total = block_exclusive_scan<kIndexThreads>(base, E, wave_tot);
+    if (c == 0) write_offsets(base, total, E, R, expert_offset, rank_offset);
+    for (int e = threadIdx.x; e < E; e += kIndexThreads) base[e] += wc[e];
+    __syncthreads();
+    rank_tile(ids, wt, base, wc, E, S, Q, s0, t0, k, nbits, token_row, recv_src_idx, recv_w);
+}
+
+// Fused path (one launch): one block of kFusedThreads per tile.  Every block
+// sweeps all T*k slots and builds, in LDS, the per-expert counts of the slots
+// before its tile (pre) and of the rest; their sum scanned over experts gives
+// the expert offsets and pre gives the tile's base rows.  The sweep is
+// redundant across blocks (each reads all ids, mostly from L2), but needs no
+// inter-block communication and no second launch.  A dependent global round
+// trip costs microseconds here, so the kernel makes exactly one: the tile's
+// weights are requested first, the sweep's loads next, and the threads that
+// load the tile's own ids keep them in LDS for the ranking.
+// LDS: pre[E], rest[E], wc[kIndexWaves][E], wave_tot[kFusedThreads/64],
+//      tile_ids[tile slots], tile_w[tile slots].
+constexpr int kFusedWeights = kMaxTileSlots / kFusedThreads;
+
+__global__ __launch_bounds__(kFusedThreads) void rows_fused_kernel(
+    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int64_t T,
+    int k, int E, int R, int tile_tokens, int nbits, int32_t* __restrict__ token_row,
+    int32_t* __restrict__ recv_src_idx, float* __restrict__ recv_w,
+    int32_t* __restrict__ expert_offset, int32_t* __restrict__ rank_offset) {
+    extern __shared__ int32_t lds[];
+    int32_t* pre = lds;
+    int32_t* rest = lds + E;
+    int32_t* wc = lds + 2 * E;
+    int32_t* wave_tot = lds + (2 + kIndexWaves) * E;
+    int32_t* tile_ids = wave_tot + kFusedThreads / kWave;
+    float* tile_w = reinterpret_cast<float*>(tile_ids + tile_tokens * k);
+    const int c = blockIdx.x;
+    const int64_t t0 = static_cast<int64_t>(c) * tile_tokens;
+    const int nt = static_cast<int>(T - t0 < tile_tokens ? T - t0 : tile_tokens);
+    const int S = nt * k;
+    const int64_t s0 = t0 * k;
+    const int Q = (S + kIndexThreads - 1) / kIndexThreads * kWave;
+    const bool want_w = recv_w != nullptr;
+
+    // The tile's weights: requested before the sweep so both share one round trip.
+    float wpre[kFusedWeights];
+#pragma unroll
+    for (int i = 0; i < kFusedWeights; ++i) {
+        const int sl = i * kFusedThreads + threadIdx.x;
+        wpre[i] = (want_w && sl < S) ? topk_weights[s0 + sl] : 0.0f;
+    }
+    for (int e = threadIdx.x; e < E; e += kFusedThreads) {
+        pre[e] = 0;
+        rest[e] = 0;
+    }
+    __syncthreads();
+    // T*k <= kFusedMaxSlots here, so 32-bit unsigned slot indices suffice.
+    const unsigned total_slots = static_cast<unsigned>(T * k);
+    const unsigned lo = static_cast<unsigned>(s0);
+    const unsigned hi = lo + static_cast<unsigned>(S);
+    for (unsigned b0 = 0; b0 < total_slots; b0 += kFusedThreads * kFusedBatch) {
+        int64_t v[kFusedBatch];
+#pragma unroll
+        for (int i = 0; i < kFusedBatch; ++i) {
+            const unsigned sl = b0 + i * kFusedThreads + threadIdx.x;
+            // scalar base + 32-bit byte offset: one VGPR of address per load
+            v[i] = sl < total_slots
+                       ? *reinterpret_cast<const int64_t*>(reinterpret_cast<const char*>(topk_idx) + sl * 8u)
+                       : -1;
+        }
+#pragma unroll
+        for (int i = 0; i < kFusedBatch; ++i) {
+            const unsigned sl = b0 + i * kFusedThreads + threadIdx.x;
+            const bool valid = v[i] >= 0 && v[i] < E;
+            if (valid) atomicAdd(sl < lo ? &pre[v[i]] : &rest[v[i]], 1);
+            if (sl >= lo && sl < hi) tile_ids[sl - lo] = valid ? static_cast<int32_t>(v[i]) : -1;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kFusedWeights; ++i) {
+        const int sl = i * kFusedThreads + threadIdx.x;
+        if (sl < S) tile_w[sl] = wpre[i];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kFusedThreads) rest[e] += pre[e];
+    __syncthreads();
+    const int total = block_exclusive_scan<kFusedThreads>(rest, E, wave_tot);
+    if (c == 0) write_offsets(rest, total, E, R, expert_offset, rank_offset);
+    for (int e = threadIdx.x; e < E; e += kFusedThreads) pre[e] += rest[e];
+    // The ranking waves pick up their slots from LDS.
+    int ids[kSlotsPerLane];
+    float wt[kSlotsPerLane];
+    {
+        const int lane = lane_id();
+        const int wave = threadIdx.x / kWave;
+        const bool ranker = threadIdx.x < kIndexThreads;
+#pragma unroll
+        for (int i = 0; i < kSlotsPerLane; ++i) {
+            const int s = wave * Q + i * kWave + lane;
+            const bool in = ranker && i * kWave < Q && s < S;
+            ids[i] = in ? tile_ids[s] : -1;
+            wt[i] = in ? tile_w[s] : 0.0f;
+        }
+    }
+    __syncthreads();
+    rank_tile(ids, wt, pre, wc, E, S, Q, s0, t0, k, nbits, token_row, recv_src_idx, recv_w);
 }
 
 __global__ void zero_offsets_kernel(int32_t* expert_offset, int E, int32_t* rank_offset, int R) {
@@ -341,15 +466,25 @@ hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weig
     }
     const int tt = index_tile_tokens(T, k);
     const int ntiles = static_cast<int>(ceil_div(T, tt));
+    const int nbits = E > 1 ? 32 - __builtin_clz(static_cast<unsigned>(E - 1)) : 0;
+    const float* w_in = recv_w ? topk_weights : nullptr;
+    float* w_out = topk_weights ? recv_w : nullptr;
+    const size_t fused_lds = (static_cast<size_t>(2 + kIndexWaves) * E + kFusedThreads / kWave +
+                              2 * static_cast<size_t>(tt) * k) * sizeof(int32_t);
+    if (T * k <= kFusedMaxSlots && fused_lds <= kFusedMaxLds) {
+        const size_t lds = fused_lds;
+        hipLaunchKernelGGL(rows_fused_kernel, dim3(ntiles), dim3(kFusedThreads), lds, stream,
+                           topk_idx, w_in, T, k, E, R, tt, nbits, token_row, recv_src_idx, w_out,
+                           expert_offset, rank_offset);
+        return hipGetLastError();
+    }
     int32_t* hist = static_cast<int32_t*>(workspace);
     hipLaunchKernelGGL(tile_hist_kernel, dim3(ntiles), dim3(kIndexThreads),
                        static_cast<size_t>(E) * sizeof(int32_t), stream, topk_idx, T, k, E, tt, hist);
-    const int nbits = E > 1 ? 32 - __builtin_clz(static_cast<unsigned>(E - 1)) : 0;
     const size_t lds = (static_cast<size_t>(1 + kIndexWaves) * E + kIndexWaves) * sizeof(int32_t);
-    hipLaunchKernelGGL(rows_kernel, dim3(ntiles), dim3(kIndexThreads), lds, stream, topk_idx,
-                       (recv_w ? topk_weights : nullptr), T, k, E, R, tt, ntiles, nbits, hist,
-                       token_row, recv_src_idx, (topk_weights ? recv_w : nullptr), expert_offset,
-                       rank_offset);
+    hipLaunchKernelGGL(rows_kernel, dim3(ntiles), dim3(kIndexThreads), lds, stream, topk_idx, w_in,
+                       T, k, E, R, tt, ntiles, nbits, hist, token_row, recv_src_idx, w_out,
+                       expert_offset, rank_offset);
     return hipGetLastError();
 }
 

@@ -18,6 +18,10 @@ constexpr int kLayoutTokensPerBlock = 256;
 constexpr int kMaxTiles = 64;
 constexpr int kMaxTileSlots = 4096;
 constexpr int kIndexThreads = 256;
+// Up to this many slots (T*k) one fused launch computes the receive order;
+// beyond it, a histogram launch feeds the ranking launch.
+constexpr int64_t kFusedMaxSlots = int64_t(1) << 18;
+constexpr size_t kFusedMaxLds = 64 * 1024;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
