@@ -20,8 +20,11 @@
 //   copy_bf16    one block per (token, 2 KB column segment), one wave per
 //                destination row: x[t] shared through L2, two 16-byte
 //                non-temporal stores per lane per row
-//   copy_fp8     same walk; per 128-channel block amax over 8 lanes, scale
-//                amax/448, E4M3FN codes, 16-byte code stores + scale stores
+//   copy_fp8     one wave per (token, 1024 channels); per 128-channel block
+//                amax over 8 lanes, scale amax/448, E4M3FN codes, 16-byte
+//                code stores + scale stores to each of the token's rows
+//   dispatch_small_{bf16,fp8}   for T*k <= kSmallSlots: the copy kernels with
+//                the receive order derived inside each block (one launch)
 #include "ep_device.h"
 #include "ep_launch.h"
 
@@ -380,6 +383,36 @@ __global__ __launch_bounds__(512) void copy_bf16_kernel(const u32x4* __restrict_
     }
 }
 
+// Quantise the 16 consecutive bf16 channels a lane holds (two 16-byte
+// vectors) as part of a 128-channel block shared by 8 aligned lanes: block
+// amax by three xor-shuffles, scale = amax / 448 (one correctly rounded fp32
+// division), codes = E4M3FN(x / scale), or all zero when the scale is 0.
+// Every lane of the wave must call it (the shuffles span the wave).
+__device__ __forceinline__ u32x4 quantize16(u32x4 a0, u32x4 a1, float& scale) {
+    float f[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_lo(a0[i]);
+        f[2 * i + 1] = bf16_hi(a0[i]);
+        f[8 + 2 * i] = bf16_lo(a1[i]);
+        f[8 + 2 * i + 1] = bf16_hi(a1[i]);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
+    const float s = amax / 448.0f;
+    u32x4 q = {0u, 0u, 0u, 0u};
+    if (s > 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) q[i / 4] |= e4m3fn_encode(f[i] / s) << (8 * (i % 4));
+    }
+    scale = s;
+    return q;
+}
+
 // FP8 copy: a lane owns 16 consecutive channels (two 16-byte bf16 vectors),
 // 8 lanes one 128-channel block, a wave 1024 channels of one token.
 __global__ __launch_bounds__(256) void copy_fp8_kernel(const u32x4* __restrict__ x,
@@ -402,26 +435,8 @@ __global__ __launch_bounds__(256) void copy_fp8_kernel(const u32x4* __restrict__
             a0 = __builtin_nontemporal_load(src);
             a1 = __builtin_nontemporal_load(src + 1);
         }
-        float f[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[2 * i] = bf16_lo(a0[i]);
-            f[2 * i + 1] = bf16_hi(a0[i]);
-            f[8 + 2 * i] = bf16_lo(a1[i]);
-            f[8 + 2 * i + 1] = bf16_hi(a1[i]);
-        }
-        float amax = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-        amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-        amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
-        amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
-        const float s = amax / 448.0f;
-        u32x4 q = {0u, 0u, 0u, 0u};
-        if (s > 0.0f) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) q[i / 4] |= e4m3fn_encode(f[i] / s) << (8 * (i % 4));
-        }
+        float s;
+        const u32x4 q = quantize16(a0, a1, s);
         const int my_row = lane < k ? token_row[t * k + lane] : -1;
         for (int j = 0; j < k; ++j) {
             const int r = read_lane(my_row, j);
@@ -432,6 +447,179 @@ __global__ __launch_bounds__(256) void copy_fp8_kernel(const u32x4* __restrict__
                 if ((lane & 7) == 0) recv_scales[static_cast<int64_t>(r) * nb + ch0 / 128] = s;
             }
         }
+    }
+}
+
+// ---- small batches: receive order and copy in one launch -------------------
+// For T*k <= kSmallSlots every copy block derives the rows of its own token:
+// it counts all T*k ids in LDS (those before the token, and all), scans the
+// totals over experts, and ranks the token's k slots among themselves.  The
+// ids are a few KB and L2-resident after the first blocks, so this costs one
+// round trip that overlaps the block's x loads, and no index launch precedes
+// the copy.  The token's first block writes its token_row / recv_src_idx /
+// recv_topk_weights; block 0 writes the offsets.
+// LDS: cnt_pre[E], cnt_all[E], wave_tot[16], own[EP_MAX_TOPK], rows[EP_MAX_TOPK].
+constexpr int kSmallMaxK = 64;
+
+__device__ int block_exclusive_scan_rt(int32_t* a, int n, int32_t* wave_tot) {
+    const int nthreads = blockDim.x;
+    const int ipt = (n + nthreads - 1) / nthreads;
+    const int b = threadIdx.x * ipt;
+    int sum = 0;
+    for (int i = 0; i < ipt; ++i)
+        if (b + i < n) sum += a[b + i];
+    int incl = sum;
+    const int lane = lane_id();
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int v = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += v;
+    }
+    const int wave = threadIdx.x / kWave;
+    if (lane == kWave - 1) wave_tot[wave] = incl;
+    __syncthreads();
+    int base = 0, total = 0;
+    for (int w = 0; w < nthreads / kWave; ++w) {
+        base += (w < wave) ? wave_tot[w] : 0;
+        total += wave_tot[w];
+    }
+    int run = base + incl - sum;
+    for (int i = 0; i < ipt; ++i)
+        if (b + i < n) {
+            const int v = a[b + i];
+            a[b + i] = run;
+            run += v;
+        }
+    __syncthreads();
+    return total;
+}
+
+// Rows of token t into rows_out[0..k) (LDS, -1 for an empty slot).  Called by
+// every thread of the block.
+__device__ void small_token_rows(const int64_t* __restrict__ topk_idx,
+                                 const float* __restrict__ topk_weights, int64_t T, int k, int E,
+                                 int R, int64_t t, bool write_maps, bool write_offs,
+                                 int32_t* __restrict__ token_row,
+                                 int32_t* __restrict__ recv_src_idx, float* __restrict__ recv_w,
+                                 int32_t* __restrict__ expert_offset,
+                                 int32_t* __restrict__ rank_offset, int32_t* lds,
+                                 int32_t* rows_out) {
+    int32_t* cnt_pre = lds;
+    int32_t* cnt_all = lds + E;
+    int32_t* wave_tot = lds + 2 * E;
+    int32_t* own = wave_tot + 16;
+    const int j = threadIdx.x;
+    // The token's weights (needed only by its first block): requested first.
+    const float wj = (write_maps && recv_w && j < k) ? topk_weights[t * k + j] : 0.0f;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        cnt_pre[e] = 0;
+        cnt_all[e] = 0;
+    }
+    __syncthreads();
+    const int total_slots = static_cast<int>(T * k);
+    const int first = static_cast<int>(t * k);
+#pragma unroll 4
+    for (int sl = threadIdx.x; sl < total_slots; sl += blockDim.x) {
+        const int64_t e = topk_idx[sl];
+        const bool valid = e >= 0 && e < E;
+        if (valid) {
+            atomicAdd(&cnt_all[e], 1);
+            if (sl < first) atomicAdd(&cnt_pre[e], 1);
+        }
+        if (sl >= first && sl < first + k) own[sl - first] = valid ? static_cast<int32_t>(e) : -1;
+    }
+    __syncthreads();
+    const int total = block_exclusive_scan_rt(cnt_all, E, wave_tot);
+    if (write_offs) write_offsets(cnt_all, total, E, R, expert_offset, rank_offset);
+    if (j < k) {
+        const int e = own[j];
+        int row = -1;
+        if (e >= 0) {
+            int before = 0;
+            for (int q = 0; q < j; ++q) before += own[q] == e;
+            row = cnt_all[e] + cnt_pre[e] + before;
+        }
+        rows_out[j] = row;
+        if (write_maps) {
+            token_row[t * k + j] = row;
+            if (row >= 0) {
+                recv_src_idx[row] = static_cast<int32_t>(t);
+                if (recv_w) recv_w[row] = wj;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// bf16, small batches: the copy_bf16 block shape, rows derived in-block.
+__global__ __launch_bounds__(512) void dispatch_small_bf16_kernel(
+    const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_weights, int64_t T, int k, int E, int R, int V, int kb,
+    int segs, u32x4* __restrict__ recv, int32_t* __restrict__ token_row,
+    int32_t* __restrict__ recv_src_idx, float* __restrict__ recv_w,
+    int32_t* __restrict__ expert_offset, int32_t* __restrict__ rank_offset) {
+    extern __shared__ int32_t lds[];
+    int32_t* rows = lds + 2 * E + 16 + kSmallMaxK;
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int64_t t = blockIdx.x / segs;
+    const int seg = static_cast<int>(blockIdx.x - t * segs);
+    const int v0 = seg * (kCopyVec * kWave) + lane;
+    u32x4 val[kCopyVec];
+#pragma unroll
+    for (int u = 0; u < kCopyVec; ++u) {
+        const int v = v0 + u * kWave;
+        if (v < V) val[u] = x[t * V + v];
+    }
+    small_token_rows(topk_idx, topk_weights, T, k, E, R, t, seg == 0, blockIdx.x == 0, token_row,
+                     recv_src_idx, recv_w, expert_offset, rank_offset, lds, rows);
+    for (int j = w; j < k; j += kb) {
+        const int r = rows[j];
+        if (r < 0) continue;
+        u32x4* dst = recv + static_cast<int64_t>(r) * V;
+#pragma unroll
+        for (int u = 0; u < kCopyVec; ++u) {
+            const int v = v0 + u * kWave;
+            if (v < V) __builtin_nontemporal_store(val[u], dst + v);
+        }
+    }
+}
+
+// FP8, small batches: block = 4 waves = (token, 4096-channel segment), each
+// wave quantises 1024 channels and stores them to every row of the token.
+__global__ __launch_bounds__(256) void dispatch_small_fp8_kernel(
+    const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_weights, int64_t T, int k, int E, int R, int H, int segs,
+    uint8_t* __restrict__ recv_q, float* __restrict__ recv_scales,
+    int32_t* __restrict__ token_row, int32_t* __restrict__ recv_src_idx,
+    float* __restrict__ recv_w, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ rank_offset) {
+    extern __shared__ int32_t lds[];
+    int32_t* rows = lds + 2 * E + 16 + kSmallMaxK;
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int64_t t = blockIdx.x / segs;
+    const int seg = static_cast<int>(blockIdx.x - t * segs);
+    const int V = H / 8;
+    const int nb = H / 128;
+    const int ch0 = seg * 4096 + w * 1024 + lane * 16;
+    const bool active = ch0 < H;
+    u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
+    if (active) {
+        const u32x4* src = x + t * V + ch0 / 8;
+        a0 = __builtin_nontemporal_load(src);
+        a1 = __builtin_nontemporal_load(src + 1);
+    }
+    small_token_rows(topk_idx, topk_weights, T, k, E, R, t, seg == 0, blockIdx.x == 0, token_row,
+                     recv_src_idx, recv_w, expert_offset, rank_offset, lds, rows);
+    float s;
+    const u32x4 q = quantize16(a0, a1, s);
+    if (!active) return;
+    for (int j = 0; j < k; ++j) {
+        const int r = rows[j];
+        if (r < 0) continue;
+        __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(recv_q + static_cast<int64_t>(r) * H + ch0));
+        if ((lane & 7) == 0) recv_scales[static_cast<int64_t>(r) * nb + ch0 / 128] = s;
     }
 }
 
@@ -485,6 +673,43 @@ hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weig
     hipLaunchKernelGGL(rows_kernel, dim3(ntiles), dim3(kIndexThreads), lds, stream, topk_idx, w_in,
                        T, k, E, R, tt, ntiles, nbits, hist, token_row, recv_src_idx, w_out,
                        expert_offset, rank_offset);
+    return hipGetLastError();
+}
+
+static size_t small_lds_bytes(int E) {
+    return (2 * static_cast<size_t>(E) + 16 + 2 * kSmallMaxK) * sizeof(int32_t);
+}
+
+bool dispatch_is_small(int64_t T, int k) { return T > 0 && T * k <= kSmallSlots; }
+
+hipError_t launch_dispatch_small_bf16(const void* x, const int64_t* topk_idx,
+                                      const float* topk_weights, int64_t T, int H, int k, int E,
+                                      int R, void* recv_x, int32_t* recv_src_idx, float* recv_w,
+                                      int32_t* expert_offset, int32_t* rank_offset,
+                                      int32_t* token_row, hipStream_t stream) {
+    const int V = H / 8;
+    const int segs = static_cast<int>(ceil_div(V, kCopyVec * kWave));
+    const int kb = k < 8 ? k : 8;
+    hipLaunchKernelGGL(dispatch_small_bf16_kernel, dim3(static_cast<unsigned>(T * segs)),
+                       dim3(kb * kWave), small_lds_bytes(E), stream, static_cast<const u32x4*>(x),
+                       topk_idx, (recv_w ? topk_weights : nullptr), T, k, E, R, V, kb, segs,
+                       static_cast<u32x4*>(recv_x), token_row, recv_src_idx,
+                       (topk_weights ? recv_w : nullptr), expert_offset, rank_offset);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_small_fp8(const void* x, const int64_t* topk_idx,
+                                     const float* topk_weights, int64_t T, int H, int k, int E,
+                                     int R, uint8_t* recv_q, float* recv_scales,
+                                     int32_t* recv_src_idx, float* recv_w,
+                                     int32_t* expert_offset, int32_t* rank_offset,
+                                     int32_t* token_row, hipStream_t stream) {
+    const int segs = static_cast<int>(ceil_div(H, 4096));
+    hipLaunchKernelGGL(dispatch_small_fp8_kernel, dim3(static_cast<unsigned>(T * segs)), dim3(256),
+                       small_lds_bytes(E), stream, static_cast<const u32x4*>(x), topk_idx,
+                       (recv_w ? topk_weights : nullptr), T, k, E, R, H, segs, recv_q, recv_scales,
+                       token_row, recv_src_idx, (topk_weights ? recv_w : nullptr), expert_offset,
+                       rank_offset);
     return hipGetLastError();
 }
 

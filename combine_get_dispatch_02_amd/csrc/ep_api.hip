@@ -128,6 +128,13 @@ int ep_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weight
                                   workspace ? workspace_bytes : 0);
     if (s != EP_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (ep::dispatch_is_small(num_tokens, num_topk))
+        return hip_status(ep::launch_dispatch_small_bf16(x, topk_idx, topk_weights, num_tokens, hidden,
+                                                         num_topk, num_experts, num_ranks, recv_x,
+                                                         recv_src_idx, recv_topk_weights,
+                                                         recv_expert_offset, recv_rank_offset,
+                                                         token_row, st),
+                          fn);
     s = hip_status(ep::launch_dispatch_index(topk_idx, topk_weights, num_tokens, num_topk,
                                              num_experts, num_ranks, recv_src_idx,
                                              recv_topk_weights, recv_expert_offset,
@@ -157,6 +164,13 @@ int ep_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_we
     if (num_tokens > 0 && (reinterpret_cast<uintptr_t>(recv_scales) & 3u))
         return fail(EP_ERR_INVALID_ARGUMENT, "%s: recv_scales must be 4-byte aligned", fn);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (ep::dispatch_is_small(num_tokens, num_topk))
+        return hip_status(ep::launch_dispatch_small_fp8(x, topk_idx, topk_weights, num_tokens, hidden,
+                                                        num_topk, num_experts, num_ranks, recv_x_fp8,
+                                                        recv_scales, recv_src_idx, recv_topk_weights,
+                                                        recv_expert_offset, recv_rank_offset,
+                                                        token_row, st),
+                          fn);
     s = hip_status(ep::launch_dispatch_index(topk_idx, topk_weights, num_tokens, num_topk,
                                              num_experts, num_ranks, recv_src_idx,
                                              recv_topk_weights, recv_expert_offset,

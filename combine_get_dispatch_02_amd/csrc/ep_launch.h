@@ -22,6 +22,9 @@ constexpr int kIndexThreads = 256;
 // beyond it, a histogram launch feeds the ranking launch.
 constexpr int64_t kFusedMaxSlots = int64_t(1) << 18;
 constexpr size_t kFusedMaxLds = 64 * 1024;
+// Up to this many slots (T*k) each copy block derives its own token's rows and
+// ep_dispatch / ep_dispatch_fp8 are a single launch.
+constexpr int64_t kSmallSlots = 2048;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
@@ -38,6 +41,20 @@ hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weig
                                  int k, int E, int R, int32_t* recv_src_idx, float* recv_w,
                                  int32_t* expert_offset, int32_t* rank_offset,
                                  int32_t* token_row, void* workspace, hipStream_t stream);
+
+// ---- small batches: receive order + copy in one launch -------------------------
+bool dispatch_is_small(int64_t T, int k);
+hipError_t launch_dispatch_small_bf16(const void* x, const int64_t* topk_idx,
+                                      const float* topk_weights, int64_t T, int H, int k, int E,
+                                      int R, void* recv_x, int32_t* recv_src_idx, float* recv_w,
+                                      int32_t* expert_offset, int32_t* rank_offset,
+                                      int32_t* token_row, hipStream_t stream);
+hipError_t launch_dispatch_small_fp8(const void* x, const int64_t* topk_idx,
+                                     const float* topk_weights, int64_t T, int H, int k, int E,
+                                     int R, uint8_t* recv_q, float* recv_scales,
+                                     int32_t* recv_src_idx, float* recv_w,
+                                     int32_t* expert_offset, int32_t* rank_offset,
+                                     int32_t* token_row, hipStream_t stream);
 
 // ---- data movement ------------------------------------------------------------
 hipError_t launch_dispatch_copy_bf16(const void* x, const int32_t* token_row, void* recv_x,

@@ -285,13 +285,40 @@ def test_edge_duplicates_and_out_of_range_ids():
 
 
 @pytest.mark.parametrize("T,k,E,R,H", [(1, 1, 1, 1, 8), (5, 1, 4, 4, 8), (64, 2, 2, 1, 24),
-                                       (257, 8, 64, 64, 64), (1000, 3, 2048, 64, 16)])
+                                       (257, 8, 64, 64, 64), (1000, 3, 2048, 64, 16),
+                                       (100, 16, 64, 8, 136),     # single-launch path, k > 8
+                                       (256, 8, 256, 8, 64),      # exactly 2048 slots
+                                       (257, 8, 256, 8, 64)])     # one token past it
 def test_edge_degenerate_shapes(T, k, E, R, H):
     rng = np.random.default_rng(T + k)
     idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int64)
     x = rng.integers(0, 0x7F00, size=(T, H)).astype(np.uint16)
     w = rng.random((T, k)).astype(np.float32)
     _run_small(idx, x, w, E, R, 1)
+
+
+@pytest.mark.parametrize("T,k,E,R,H", [(100, 16, 64, 8, 1024), (256, 8, 256, 16, 4224),
+                                       (257, 8, 256, 16, 4224), (3, 1, 8, 2, 128)])
+def test_fp8_dispatch_paths(T, k, E, R, H):
+    """FP8 dispatch on both sides of the single-launch threshold (2048 slots),
+    with row widths that leave waves and segments partly idle."""
+    rng = np.random.default_rng(T * k + H)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int64)
+    x = random_x = (rng.standard_normal((T, H)).astype(np.float32) * 3)
+    from combine_get_dispatch_02_amd.workloads import bf16_bits
+    x = bf16_bits(random_x)
+    w = rng.random((T, k)).astype(np.float32)
+    ref = oracle.dispatch_fp8(x, idx, w, E, R)
+    N = int(ref["recv_expert_offset"][-1])
+    f = ep.ep_dispatch_fp8(dev_bf16(x), torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV),
+                           E, R, out=prefilled_dispatch_out(T, k, H, E, R, True))
+    torch.cuda.synchronize()
+    check_index_maps(f, ref, N)
+    q = f["recv_x_fp8"].cpu().numpy()
+    sc = f["recv_scales"].cpu().numpy()
+    np.testing.assert_array_equal(sc[:N].view(np.uint32), ref["recv_scales"][:N].view(np.uint32))
+    assert fp8_ulp_ok(q[:N], ref["recv_x_fp8"][:N])
+    assert np.all(q[N:] == SENT8)
 
 
 def test_edge_fp8_special_blocks():
@@ -322,6 +349,40 @@ def test_edge_fp8_special_blocks():
     np.testing.assert_array_equal(q, ref["recv_x_fp8"][:N])
     r2 = ref["token_row"][2, 0]
     assert 0 < s[r2, 0] < np.finfo(np.float32).tiny          # denormal scale survived
+
+
+@pytest.mark.parametrize("T,k,E,R,H,mask", [
+    (40000, 8, 256, 8, 64, 0.0),      # T*k > 2^18: histogram launch + ranking launch
+    (33000, 8, 64, 8, 64, 0.05),      # same path, masked slots, ragged last tile
+    (3000, 6, 2048, 64, 128, 0.02),   # many experts and ranks (fused path, large LDS)
+    (20000, 16, 2048, 64, 16, 0.0),   # many experts, T*k > 2^18, k > 8
+])
+def test_parity_receive_order_paths(T, k, E, R, H, mask):
+    """Both receive-order paths (one fused launch up to 2^18 slots, two
+    launches above) against the oracle, element by element."""
+    _say(f"[parity-paths] T={T} k={k} E={E} R={R} H={H} mask={mask}")
+    rng = np.random.default_rng(T + E)
+    idx = np.argsort(rng.random((T, E), dtype=np.float32), axis=1)[:, :k].astype(np.int64)
+    if mask:
+        idx = mask_slots(idx, mask, 3)
+    x = rng.integers(0, 0x7F00, size=(T, H)).astype(np.uint16)
+    w = rng.random((T, k)).astype(np.float32)
+    P = min(8, R)
+    wl = dataclasses.replace(CONFIGS["tiny"], T=T, H=H, k=k, E=E, R=R, P=P)
+    ref_l = oracle.layout(idx, E, R, P)
+    ref_d = oracle.dispatch(x, idx, w, E, R)
+    N = int(ref_d["recv_expert_offset"][-1])
+    xd, idxd, wd = dev_bf16(x), torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV)
+    check_layout(gpu_layout(idxd, wl), ref_l)
+    out = prefilled_dispatch_out(T, k, H, E, R, fp8=False)
+    d = ep.ep_dispatch(xd, idxd, wd, E, R, out=out)
+    torch.cuda.synchronize()
+    check_index_maps(d, ref_d, N)
+    rx = host_bits(d["recv_x"])
+    np.testing.assert_array_equal(rx[:N], ref_d["recv_x"][:N])
+    assert np.all(rx[N:] == SENT16)
+    got = host_bits(ep.ep_combine(d["recv_x"], d["token_row"], wd, num_rows=N))
+    np.testing.assert_array_equal(got, oracle.combine(ref_d["recv_x"], ref_d["token_row"], w, num_rows=N))
 
 
 def test_combine_skips_rows_outside_num_rows():
