@@ -50,13 +50,15 @@ def _load() -> ctypes.CDLL:
     lib.oracle_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P]
     lib.oracle_dispatch_fp8.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P]
     lib.oracle_combine.argtypes = [P, i64, P, P, i64, i32, i32, P]
+    lib.oracle_dispatch_cached.argtypes = [P, P, i64, i32, i32, P, i64]
+    lib.oracle_dispatch_fp8_cached.argtypes = [P, P, i64, i32, i32, P, P, i64]
     lib.oracle_quantize_row.argtypes = [P, i32, P, P]
     lib.oracle_e4m3_encode_array.argtypes = [P, i64, P]
     lib.oracle_bf16_rne_array.argtypes = [P, i64, P]
     lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3_decode.restype = ctypes.c_float
     for f in ("oracle_layout", "oracle_dispatch", "oracle_dispatch_fp8", "oracle_combine",
-              "oracle_quantize_row"):
+              "oracle_quantize_row", "oracle_dispatch_cached", "oracle_dispatch_fp8_cached"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -73,7 +75,7 @@ def _use_library(path: Optional[str]) -> None:
         lib = ctypes.CDLL(path)
         for f in ("oracle_layout", "oracle_dispatch", "oracle_dispatch_fp8", "oracle_combine",
                   "oracle_quantize_row", "oracle_e4m3_encode_array", "oracle_bf16_rne_array",
-                  "oracle_e4m3_decode"):
+                  "oracle_e4m3_decode", "oracle_dispatch_cached", "oracle_dispatch_fp8_cached"):
             getattr(lib, f).argtypes = getattr(_lib, f).argtypes
             getattr(lib, f).restype = getattr(_lib, f).restype
         _lib = lib
@@ -156,6 +158,32 @@ def dispatch_fp8(x: np.ndarray, topk_idx: np.ndarray, topk_weights: Optional[np.
     return dict(recv_x_fp8=recv_q, recv_scales=recv_s, recv_src_idx=src,
                 recv_topk_weights=recv_w, recv_expert_offset=eoff, recv_rank_offset=roff,
                 token_row=trow)
+
+
+def dispatch_cached(x: np.ndarray, token_row: np.ndarray, num_rows: int,
+                    recv_x: Optional[np.ndarray] = None):
+    """recv_x[token_row[t,j]] = x[t] for rows in [0, num_rows); other rows of
+    recv_x (zeros, or the given array) are left as they are."""
+    x = _c(x, np.uint16)
+    trow = _c(token_row, np.int32)
+    T, k = trow.shape
+    H = x.shape[1]
+    out = np.zeros((num_rows, H), np.uint16) if recv_x is None else recv_x
+    rc = _load().oracle_dispatch_cached(_p(x), _p(trow), T, H, k, _p(out), num_rows)
+    _check(rc, "oracle_dispatch_cached")
+    return out
+
+
+def dispatch_fp8_cached(x: np.ndarray, token_row: np.ndarray, num_rows: int):
+    x = _c(x, np.uint16)
+    trow = _c(token_row, np.int32)
+    T, k = trow.shape
+    H = x.shape[1]
+    q = np.zeros((num_rows, H), np.uint8)
+    s = np.full((num_rows, H // 128), np.nan, np.float32)
+    rc = _load().oracle_dispatch_fp8_cached(_p(x), _p(trow), T, H, k, _p(q), _p(s), num_rows)
+    _check(rc, "oracle_dispatch_fp8_cached")
+    return q, s
 
 
 def quantize_row(xrow: np.ndarray):

@@ -313,6 +313,44 @@ int oracle_dispatch_fp8(const uint16_t* x, const int64_t* topk_idx, const float*
     return ORC_OK;
 }
 
+/* Cached dispatch: reuse the receive map of an earlier dispatch (page
+ * "[Not ready] MSCCLPP EP implementation #852", PR body "Scope / Internode
+ * HT": cached_notify reuses a previous dispatch's layout for a repeat
+ * dispatch).  For every slot whose row r = token_row[t,j] lies in
+ * [0, num_rows): recv_x[r, :] = x[t, :]; other slots are skipped. */
+int oracle_dispatch_cached(const uint16_t* x, const int32_t* token_row, int64_t T, int H, int k,
+                           uint16_t* recv_x, int64_t num_rows)
+{
+    if (T < 0 || H < 1 || k < 1 || num_rows < 0) return ORC_EINVAL;
+    if (T > 0 && (!x || !token_row || (num_rows > 0 && !recv_x))) return ORC_EINVAL;
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int32_t row = token_row[t * k + j];
+            if (row < 0 || (int64_t)row >= num_rows) continue;
+            memcpy(recv_x + (int64_t)row * H, x + t * (int64_t)H, sizeof(uint16_t) * (size_t)H);
+        }
+    return ORC_OK;
+}
+
+/* Cached FP8 dispatch: the per-token cast of oracle_quantize_row written to
+ * every row of the reused map that lies in [0, num_rows). */
+int oracle_dispatch_fp8_cached(const uint16_t* x, const int32_t* token_row, int64_t T, int H,
+                               int k, uint8_t* recv_x_fp8, float* recv_scales, int64_t num_rows)
+{
+    if (T < 0 || H < 128 || H % 128 != 0 || k < 1 || num_rows < 0) return ORC_EINVAL;
+    if (T > 0 && (!x || !token_row || (num_rows > 0 && (!recv_x_fp8 || !recv_scales))))
+        return ORC_EINVAL;
+    const int nb = H / 128;
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int32_t row = token_row[t * k + j];
+            if (row < 0 || (int64_t)row >= num_rows) continue;
+            oracle_quantize_row(x + t * (int64_t)H, H, recv_x_fp8 + (int64_t)row * H,
+                                recv_scales + (int64_t)row * nb);
+        }
+    return ORC_OK;
+}
+
 /* ep_combine: for each token t and channel h, an fp32 accumulator starts at
  * +0 and takes one fused multiply-add per valid slot in fixed top-k (j)
  * order:  acc = fma(w[t,j], y[token_row[t,j], h], acc);  out = bf16_RNE(acc).

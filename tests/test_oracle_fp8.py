@@ -154,3 +154,13 @@ def test_fp8_dispatch_rows_hold_token_cast():
         for r in d["token_row"][t]:
             np.testing.assert_array_equal(d["recv_x_fp8"][r], q)
             np.testing.assert_array_equal(d["recv_scales"][r], s)
+
+
+def test_fp8_cached_dispatch_matches_fp8_dispatch():
+    wl = CONFIGS["ll_fp8"].scaled(T=20, H=384)
+    x, idx, w = make_workload(wl)
+    d = oracle.dispatch_fp8(x, idx, w, wl.E, wl.R)
+    N = int(d["recv_expert_offset"][-1])
+    q, s = oracle.dispatch_fp8_cached(x, d["token_row"], N)
+    np.testing.assert_array_equal(q, d["recv_x_fp8"][:N])
+    np.testing.assert_array_equal(s.view(np.uint32), d["recv_scales"][:N].view(np.uint32))

@@ -183,3 +183,27 @@ def test_invalid_arguments(args):
     idx = np.zeros((2, 2), np.int64)
     with pytest.raises(oracle.OracleError):
         oracle.layout(idx, args["E"], args["R"], args["P"])
+
+
+@pytest.mark.parametrize("case", range(len(ROUTINGS)))
+def test_cached_dispatch_reproduces_dispatch(case):
+    """Reusing a dispatch's own map reproduces its receive buffer; the same
+    scatter written with numpy fancy indexing (a library routine) agrees,
+    including for a map with rows outside [0, num_rows)."""
+    T, k, E, R, P, mf, dup, bad = ROUTINGS[case]
+    idx = _random_idx(T, k, E, mf, dup, bad, case)
+    x = np.random.default_rng(case).integers(0, 65535, size=(T, 24)).astype(np.uint16)
+    d = oracle.dispatch(x, idx, None, E, R)
+    N = int(d["recv_expert_offset"][-1])
+    got = oracle.dispatch_cached(x, d["token_row"], N)
+    np.testing.assert_array_equal(got, d["recv_x"][:N])
+    # a perturbed map: some rows pushed out of range, a few set to -1
+    rng = np.random.default_rng(100 + case)
+    trow = d["token_row"].copy()
+    trow[rng.random(trow.shape) < 0.2] += N
+    rows = max(N, 1)
+    ref = np.zeros((rows, 24), np.uint16)
+    tt = np.repeat(np.arange(T), k).reshape(T, k)
+    ok = (trow >= 0) & (trow < rows)
+    ref[trow[ok]] = x[tt[ok]]
+    np.testing.assert_array_equal(oracle.dispatch_cached(x, trow, rows), ref)

@@ -34,6 +34,12 @@ def _row_pins():
         tl.test_hand_worked_example(name)
 
 
+def _cached_pins():
+    for i in range(len(tl.ROUTINGS)):
+        tl.test_cached_dispatch_reproduces_dispatch(i)
+    tf.test_fp8_cached_dispatch_matches_fp8_dispatch()
+
+
 def _fp8_pins():
     tf.test_decode_all_codes_against_torch()
     tf.test_encode_roundtrips_every_finite_code()
@@ -108,6 +114,16 @@ MUTATIONS = {
     "combine_no_range_guard": ("if (row < 0 || (int64_t)row >= num_rows) continue;\n                acc",
                                "if (row < 0) continue;\n                if (row >= num_rows) row = num_rows - 1;\n                acc",
                                _combine_pins),
+    # cached dispatch
+    "cached_no_range_guard": ("if (row < 0 || (int64_t)row >= num_rows) continue;\n            memcpy(recv_x",
+                              "if (row < 0) continue;\n            if (row >= num_rows) row = num_rows - 1;\n            memcpy(recv_x",
+                              _cached_pins),
+    "cached_wrong_source": ("memcpy(recv_x + (int64_t)row * H, x + t * (int64_t)H, sizeof(uint16_t) * (size_t)H);\n        }\n    return ORC_OK;\n}\n\n/* Cached FP8",
+                            "memcpy(recv_x + (int64_t)row * H, x + (T - 1 - t) * (int64_t)H, sizeof(uint16_t) * (size_t)H);\n        }\n    return ORC_OK;\n}\n\n/* Cached FP8",
+                            _cached_pins),
+    "cached_fp8_scale_row": ("recv_scales + (int64_t)row * nb);\n        }\n    return ORC_OK;",
+                             "recv_scales + (int64_t)t * nb);\n        }\n    return ORC_OK;",
+                             _cached_pins),
     "bf16_widen_shift": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;", _combine_pins),
 }
 
@@ -131,5 +147,5 @@ def test_planted_mistake_is_caught(name, tmp_path):
 
 
 def test_unmutated_oracle_passes_all_pins():
-    for pins in (_layout_pins, _row_pins, _fp8_pins, _combine_pins):
+    for pins in (_layout_pins, _row_pins, _fp8_pins, _combine_pins, _cached_pins):
         pins()
