@@ -136,6 +136,49 @@ def cpu_baseline(wl, x, idx, w, budget_s):
     }
 
 
+def graph_mode(args, wl, ep, torch, np, idxd, xd, wd, lay, ws_l, disp, ws_d, comb, fp8):
+    """Eager vs HIP-graph replay of one whole step, caches left warm."""
+    E, R, P, N = wl.E, wl.R, wl.P, wl.T * wl.k
+
+    def body():
+        ep.ep_get_dispatch_layout(idxd, E, R, P, out=lay, workspace=ws_l)
+        ep.ep_dispatch(xd, idxd, wd, E, R, out=disp, workspace=ws_d)
+        ep.ep_combine(disp["recv_x"], disp["token_row"], wd, num_rows=N, out=comb)
+        ep.ep_dispatch_fp8(xd, idxd, wd, E, R, out=fp8, workspace=ws_d)
+
+    for _ in range(max(args.warmup, 3)):
+        body()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            body()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / args.steps
+
+    eager_us = timed(body)
+    graph_us = timed(g.replay)
+    print(json.dumps({"mode": "graph", "workload": wl.describe(), "steps": args.steps,
+                      "eager_us_per_step": round(eager_us, 2), "graph_us_per_step": round(graph_us, 2),
+                      "speedup": round(eager_us / graph_us, 3),
+                      "note": "layout + dispatch + combine + FP8 dispatch back to back, caches warm"}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +188,10 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between phases")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="instead of the headline: time one whole step (layout, dispatch, combine, "
+                         "FP8 dispatch; no cache eviction) replayed from a captured HIP graph "
+                         "against the same step launched eagerly")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after the timed steps, run 4 plain 256 MiB device copies (a known-size "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -222,6 +269,10 @@ def main():
 
     def events():
         return [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+
+    if args.graph:
+        graph_mode(args, wl, ep, torch, np, idxd, xd, wd, lay, ws_l, disp, ws_d, comb, fp8)
+        return
 
     for i in range(args.warmup):
         step(i, events())

@@ -359,8 +359,8 @@ constexpr int kCopyVec = 2;
 
 __global__ __launch_bounds__(512) void copy_bf16_kernel(const u32x4* __restrict__ x,
                                                         const int32_t* __restrict__ token_row,
-                                                        u32x4* __restrict__ recv, int V, int k,
-                                                        int kb, int segs) {
+                                                        u32x4* __restrict__ recv, int64_t num_rows,
+                                                        int V, int k, int kb, int segs) {
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int64_t t = blockIdx.x / segs;
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(512) void copy_bf16_kernel(const u32x4* __restrict_
     }
     for (int j = w; j < k; j += kb) {
         const int r = token_row[t * k + j];
-        if (r < 0) continue;
+        if (r < 0 || r >= num_rows) continue;
         u32x4* dst = recv + static_cast<int64_t>(r) * V;
 #pragma unroll
         for (int u = 0; u < kCopyVec; ++u) {
@@ -418,9 +418,9 @@ __device__ __forceinline__ u32x4 quantize16(u32x4 a0, u32x4 a1, float& scale) {
 __global__ __launch_bounds__(256) void copy_fp8_kernel(const u32x4* __restrict__ x,
                                                        const int32_t* __restrict__ token_row,
                                                        uint8_t* __restrict__ recv_q,
-                                                       float* __restrict__ recv_scales, int H,
-                                                       int k, int tiles_per_token,
-                                                       int64_t num_tiles) {
+                                                       float* __restrict__ recv_scales,
+                                                       int64_t num_rows, int H, int k,
+                                                       int tiles_per_token, int64_t num_tiles) {
     const int lane = lane_id();
     const int V = H / 8;
     const int nb = H / 128;
@@ -437,7 +437,8 @@ __global__ __launch_bounds__(256) void copy_fp8_kernel(const u32x4* __restrict__
         }
         float s;
         const u32x4 q = quantize16(a0, a1, s);
-        const int my_row = lane < k ? token_row[t * k + lane] : -1;
+        int my_row = lane < k ? token_row[t * k + lane] : -1;
+        if (my_row >= num_rows) my_row = -1;
         for (int j = 0; j < k; ++j) {
             const int r = read_lane(my_row, j);
             if (r < 0) continue;
@@ -714,19 +715,20 @@ hipError_t launch_dispatch_small_fp8(const void* x, const int64_t* topk_idx,
 }
 
 hipError_t launch_dispatch_copy_bf16(const void* x, const int32_t* token_row, void* recv_x,
-                                     int64_t T, int H, int k, hipStream_t stream) {
+                                     int64_t num_rows, int64_t T, int H, int k,
+                                     hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
     const int segs = static_cast<int>(ceil_div(V, kCopyVec * kWave));
     const int kb = k < 8 ? k : 8;
     hipLaunchKernelGGL(copy_bf16_kernel, dim3(static_cast<unsigned>(T * segs)), dim3(kb * kWave), 0,
-                       stream, static_cast<const u32x4*>(x), token_row, static_cast<u32x4*>(recv_x), V,
-                       k, kb, segs);
+                       stream, static_cast<const u32x4*>(x), token_row, static_cast<u32x4*>(recv_x),
+                       num_rows, V, k, kb, segs);
     return hipGetLastError();
 }
 
 hipError_t launch_dispatch_copy_fp8(const void* x, const int32_t* token_row, uint8_t* recv_q,
-                                    float* recv_scales, int64_t T, int H, int k,
+                                    float* recv_scales, int64_t num_rows, int64_t T, int H, int k,
                                     hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int tiles_per_token = static_cast<int>(ceil_div(H, 1024));
@@ -734,7 +736,7 @@ hipError_t launch_dispatch_copy_fp8(const void* x, const int32_t* token_row, uin
     const int64_t blocks = ceil_div(num_tiles, 4);
     const unsigned grid = static_cast<unsigned>(blocks < (1 << 30) ? blocks : (1 << 30));
     hipLaunchKernelGGL(copy_fp8_kernel, dim3(grid), dim3(256), 0, stream,
-                       static_cast<const u32x4*>(x), token_row, recv_q, recv_scales, H, k,
+                       static_cast<const u32x4*>(x), token_row, recv_q, recv_scales, num_rows, H, k,
                        tiles_per_token, num_tiles);
     return hipGetLastError();
 }

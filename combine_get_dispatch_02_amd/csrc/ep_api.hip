@@ -141,8 +141,8 @@ int ep_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weight
                                              recv_rank_offset, token_row, workspace, st),
                    fn);
     if (s != EP_OK) return s;
-    return hip_status(ep::launch_dispatch_copy_bf16(x, token_row, recv_x, num_tokens, hidden,
-                                                    num_topk, st),
+    return hip_status(ep::launch_dispatch_copy_bf16(x, token_row, recv_x, num_tokens * num_topk,
+                                                    num_tokens, hidden, num_topk, st),
                       fn);
 }
 
@@ -178,7 +178,53 @@ int ep_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_we
                    fn);
     if (s != EP_OK) return s;
     return hip_status(ep::launch_dispatch_copy_fp8(x, token_row, recv_x_fp8, recv_scales,
-                                                   num_tokens, hidden, num_topk, st),
+                                                   num_tokens * num_topk, num_tokens, hidden,
+                                                   num_topk, st),
+                      fn);
+}
+
+int ep_dispatch_cached(const void* x, const int32_t* token_row, int64_t num_tokens, int hidden,
+                       int num_topk, void* recv_x, int64_t recv_rows, void* stream) {
+    const char* fn = "ep_dispatch_cached";
+    if (num_tokens < 0 || recv_rows < 0)
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: num_tokens and recv_rows must be >= 0", fn);
+    if (num_topk < 1) return fail(EP_ERR_INVALID_ARGUMENT, "%s: num_topk < 1", fn);
+    if (num_topk > EP_MAX_TOPK) return fail(EP_ERR_UNSUPPORTED, "%s: num_topk > %d", fn, EP_MAX_TOPK);
+    if (hidden < 8 || hidden % 8 != 0)
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: hidden must be a positive multiple of 8", fn);
+    if (num_tokens > 0 && (!x || !token_row))
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: a required pointer is NULL", fn);
+    if (num_tokens > 0 && recv_rows > 0 && !recv_x)
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: recv_x is NULL", fn);
+    if (num_tokens > 0 && (!aligned16(x) || (recv_rows > 0 && !aligned16(recv_x))))
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: x and recv_x must be 16-byte aligned", fn);
+    if (num_tokens == 0 || recv_rows == 0) return EP_OK;
+    return hip_status(ep::launch_dispatch_copy_bf16(x, token_row, recv_x, recv_rows, num_tokens,
+                                                    hidden, num_topk, static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+int ep_dispatch_fp8_cached(const void* x, const int32_t* token_row, int64_t num_tokens,
+                           int hidden, int num_topk, uint8_t* recv_x_fp8, float* recv_scales,
+                           int64_t recv_rows, void* stream) {
+    const char* fn = "ep_dispatch_fp8_cached";
+    if (num_tokens < 0 || recv_rows < 0)
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: num_tokens and recv_rows must be >= 0", fn);
+    if (num_topk < 1) return fail(EP_ERR_INVALID_ARGUMENT, "%s: num_topk < 1", fn);
+    if (num_topk > EP_MAX_TOPK) return fail(EP_ERR_UNSUPPORTED, "%s: num_topk > %d", fn, EP_MAX_TOPK);
+    if (hidden < 128 || hidden % 128 != 0)
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: hidden must be a positive multiple of 128", fn);
+    if (num_tokens > 0 && (!x || !token_row))
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: a required pointer is NULL", fn);
+    if (num_tokens > 0 && recv_rows > 0 && (!recv_x_fp8 || !recv_scales))
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: recv_x_fp8 / recv_scales is NULL", fn);
+    if (num_tokens > 0 && (!aligned16(x) || (recv_rows > 0 && (!aligned16(recv_x_fp8) ||
+                                                               (reinterpret_cast<uintptr_t>(recv_scales) & 3u)))))
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: misaligned x / recv_x_fp8 / recv_scales", fn);
+    if (num_tokens == 0 || recv_rows == 0) return EP_OK;
+    return hip_status(ep::launch_dispatch_copy_fp8(x, token_row, recv_x_fp8, recv_scales, recv_rows,
+                                                   num_tokens, hidden, num_topk,
+                                                   static_cast<hipStream_t>(stream)),
                       fn);
 }
 

@@ -57,10 +57,13 @@ hipError_t launch_dispatch_small_fp8(const void* x, const int64_t* topk_idx,
                                      int32_t* token_row, hipStream_t stream);
 
 // ---- data movement ------------------------------------------------------------
+// Copy kernels: every slot whose row lies in [0, num_rows) receives x[t]
+// (bf16) or its FP8 cast; other slots are skipped.
 hipError_t launch_dispatch_copy_bf16(const void* x, const int32_t* token_row, void* recv_x,
-                                     int64_t T, int H, int k, hipStream_t stream);
+                                     int64_t num_rows, int64_t T, int H, int k,
+                                     hipStream_t stream);
 hipError_t launch_dispatch_copy_fp8(const void* x, const int32_t* token_row, uint8_t* recv_q,
-                                    float* recv_scales, int64_t T, int H, int k,
+                                    float* recv_scales, int64_t num_rows, int64_t T, int H, int k,
                                     hipStream_t stream);
 hipError_t launch_combine(const void* expert_out, int64_t num_rows, const int32_t* token_row,
                           const float* topk_weights, int64_t T, int H, int k, void* out,

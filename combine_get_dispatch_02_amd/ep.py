@@ -52,7 +52,10 @@ def lib() -> ctypes.CDLL:
     L.ep_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, sz, P]
     L.ep_dispatch_fp8.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, sz, P]
     L.ep_combine.argtypes = [P, i64, P, P, i64, i32, i32, P, P]
-    for f in ("ep_get_dispatch_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_combine"):
+    L.ep_dispatch_cached.argtypes = [P, P, i64, i32, i32, P, i64, P]
+    L.ep_dispatch_fp8_cached.argtypes = [P, P, i64, i32, i32, P, P, i64, P]
+    for f in ("ep_get_dispatch_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_combine",
+              "ep_dispatch_cached", "ep_dispatch_fp8_cached"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -201,6 +204,52 @@ def ep_dispatch_fp8(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: Optio
             _ptr(out.get("recv_rank_offset")), _ptr(out["token_row"]), _ptr(ws), ws.numel(),
             _stream(dev))
     _check(st, "ep_dispatch_fp8")
+    return out
+
+
+def ep_dispatch_cached(x: torch.Tensor, token_row: torch.Tensor, recv_rows: int, *,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Repeat bf16 dispatch with a saved map: recv_x[token_row[t, j]] = x[t]
+    for rows in [0, recv_rows).  Returns recv_x [recv_rows, H] bf16 (rows
+    no slot maps to are left as they were: uninitialised unless `out` is given)."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    _need(token_row, "token_row", torch.int32, dev)
+    T, H = x.shape
+    k = token_row.shape[1]
+    if token_row.shape[0] != T:
+        raise ValueError("x and token_row disagree on num_tokens")
+    if out is None:
+        out = torch.empty((recv_rows, H), dtype=torch.bfloat16, device=dev)
+    elif tuple(out.shape) != (recv_rows, H):
+        raise ValueError("out must be [recv_rows, H]")
+    else:
+        _need(out, "out", torch.bfloat16, dev)
+    with torch.cuda.device(dev):
+        st = lib().ep_dispatch_cached(_ptr(x), _ptr(token_row), T, H, k, _ptr(out), recv_rows,
+                                      _stream(dev))
+    _check(st, "ep_dispatch_cached")
+    return out
+
+
+def ep_dispatch_fp8_cached(x: torch.Tensor, token_row: torch.Tensor, recv_rows: int, *,
+                           out: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    """Repeat FP8 dispatch with a saved map: recv_x_fp8 [recv_rows, H] codes and
+    recv_scales [recv_rows, H/128]."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    _need(token_row, "token_row", torch.int32, dev)
+    T, H = x.shape
+    k = token_row.shape[1]
+    if token_row.shape[0] != T:
+        raise ValueError("x and token_row disagree on num_tokens")
+    if out is None:
+        out = dict(recv_x_fp8=torch.empty((recv_rows, H), dtype=torch.uint8, device=dev),
+                   recv_scales=torch.empty((recv_rows, H // 128), dtype=torch.float32, device=dev))
+    with torch.cuda.device(dev):
+        st = lib().ep_dispatch_fp8_cached(_ptr(x), _ptr(token_row), T, H, k, _ptr(out["recv_x_fp8"]),
+                                          _ptr(out["recv_scales"]), recv_rows, _stream(dev))
+    _check(st, "ep_dispatch_fp8_cached")
     return out
 
 

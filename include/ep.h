@@ -161,6 +161,32 @@ int ep_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_we
                     void* stream);
 
 /* ---------------------------------------------------------------------------
+ * ep_dispatch_cached / ep_dispatch_fp8_cached -- repeat dispatch that reuses
+ * the receive map of an earlier ep_dispatch / ep_dispatch_fp8 with the same
+ * routing (the cached_notify of page #852, "Scope / Internode HT": a repeat
+ * dispatch skips the layout and count exchange).  No receive-order work is
+ * done: for every slot (t, j) whose row r = token_row[t, j] lies in
+ * [0, recv_rows), row r receives x[t] (bf16, bit for bit) or its FP8 cast
+ * (codes and scales exactly as ep_dispatch_fp8 computes them).  Slots with
+ * any other row, including -1, are skipped, so no map can make the kernel
+ * write outside the recv_rows rows given.  Other rows are not written.
+ *
+ *   x           [T, H]          bf16  in (16-byte aligned)
+ *   token_row   [T, k]          int32 in (an earlier dispatch's output)
+ *   recv_x      [recv_rows, H]  bf16  out (16-byte aligned)
+ *   recv_x_fp8  [recv_rows, H]  uint8 out (16-byte aligned), recv_scales
+ *               [recv_rows, H/128] fp32 out (FP8 variant)
+ * Requires H % 8 == 0 (bf16) or H % 128 == 0 (FP8), 1 <= k <= EP_MAX_TOPK.
+ * No workspace.  T == 0 or recv_rows == 0 enqueues nothing.
+ * ------------------------------------------------------------------------- */
+int ep_dispatch_cached(const void* x, const int32_t* token_row, int64_t num_tokens, int hidden,
+                       int num_topk, void* recv_x, int64_t recv_rows, void* stream);
+
+int ep_dispatch_fp8_cached(const void* x, const int32_t* token_row, int64_t num_tokens,
+                           int hidden, int num_topk, uint8_t* recv_x_fp8, float* recv_scales,
+                           int64_t recv_rows, void* stream);
+
+/* ---------------------------------------------------------------------------
  * ep_combine -- gather each token's expert outputs back and sum them weighted
  * by topk_weights (intranode combine of "Scope / Intranode", consuming the
  * receiver-side map token_row that dispatch produced).  For every t, h:

@@ -116,3 +116,31 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ep, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         ep.lib()
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), EINVAL), (dict(rows=-1), EINVAL), (dict(k=0), EINVAL), (dict(k=65), EUNSUP),
+    (dict(H=4), EINVAL), (dict(x=None), EINVAL), (dict(trow=None), EINVAL), (dict(recv=None), EINVAL),
+    (dict(x=ctypes.c_void_p(0x100008)), EINVAL), (dict(recv=ctypes.c_void_p(0x100004)), EINVAL),
+    (dict(T=0), OK), (dict(rows=0, recv=None), OK),
+])
+def test_cached_dispatch_rejects(fp8, kw, code):
+    a = dict(x=FAKE, trow=FAKE, T=16, H=256, k=2, recv=FAKE, scales=FAKE, rows=32)
+    a.update(kw)
+    L = ep.lib()
+    if fp8:
+        st = L.ep_dispatch_fp8_cached(a["x"], a["trow"], a["T"], a["H"], a["k"], a["recv"], a["scales"],
+                                      a["rows"], None)
+    else:
+        st = L.ep_dispatch_cached(a["x"], a["trow"], a["T"], a["H"], a["k"], a["recv"], a["rows"], None)
+    assert st == code
+
+
+@pytest.mark.parametrize("kw", [dict(H=200), dict(scales=None), dict(scales=ctypes.c_void_p(0x100002))])
+def test_fp8_cached_specific_rejects(kw):
+    a = dict(x=FAKE, trow=FAKE, T=16, H=256, k=2, recv=FAKE, scales=FAKE, rows=32)
+    a.update(kw)
+    st = ep.lib().ep_dispatch_fp8_cached(a["x"], a["trow"], a["T"], a["H"], a["k"], a["recv"],
+                                         a["scales"], a["rows"], None)
+    assert st == EINVAL
