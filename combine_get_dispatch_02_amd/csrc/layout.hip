@@ -4,7 +4,8 @@
 // PR body "Scope / Intranode" (get_dispatch_layout) and "Scope / Internode
 // HT" (the per-RDMA-rank count, here a group of P consecutive ranks).
 //
-// Two launches, no atomics on global memory and no zero-fill:
+// Two launches, no atomics on global memory and no zero-fill (one when the
+// batch fits a single block of 256 tokens):
 //   1. layout_partial: one token per thread, 256 tokens per block.  Each block
 //      builds its expert / rank / group histograms in LDS, writes the
 //      is_token_in_rank rows of its tokens, and stores its histograms in the
@@ -17,9 +18,14 @@
 namespace ep {
 namespace {
 
+// kFinal: the whole batch is this one block (T <= kLayoutTokensPerBlock), so
+// its histograms are the final counts and no reduce launch follows.
+template <bool kFinal>
 __global__ __launch_bounds__(kLayoutTokensPerBlock) void layout_partial_kernel(
     const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, int P,
-    uint8_t* __restrict__ in_rank, int32_t* __restrict__ partial) {
+    uint8_t* __restrict__ in_rank, int32_t* __restrict__ partial,
+    int32_t* __restrict__ per_expert, int32_t* __restrict__ per_rank,
+    int32_t* __restrict__ per_group) {
     extern __shared__ int32_t lds[];
     const int G = R / P;
     const int epr = E / R;
@@ -63,6 +69,17 @@ __global__ __launch_bounds__(kLayoutTokensPerBlock) void layout_partial_kernel(
         const int r = i - tl * R;
         out[i] = static_cast<uint8_t>((masks[tl] >> r) & 1);
     }
+    if (kFinal) {
+        for (int i = threadIdx.x; i < nh; i += blockDim.x) {
+            if (i < E)
+                per_expert[i] = lds[i];
+            else if (i < E + R)
+                per_rank[i - E] = lds[i];
+            else if (per_group)
+                per_group[i - E - R] = lds[i];
+        }
+        return;
+    }
     int32_t* p = partial + static_cast<int64_t>(blockIdx.x) * nh;
     for (int i = threadIdx.x; i < nh; i += blockDim.x) p[i] = lds[i];
 }
@@ -100,12 +117,18 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R
     const int nh = E + R + G;
     const int64_t nblk = ceil_div(T, kLayoutTokensPerBlock);
     int32_t* partial = static_cast<int32_t*>(workspace);
+    const size_t lds = (static_cast<size_t>((nh + 1) & ~1)) * sizeof(int32_t) +
+                       kLayoutTokensPerBlock * sizeof(uint64_t);
+    if (nblk == 1) {
+        hipLaunchKernelGGL(layout_partial_kernel<true>, dim3(1), dim3(kLayoutTokensPerBlock), lds,
+                           stream, topk_idx, T, k, E, R, P, in_rank, partial, per_expert, per_rank,
+                           per_group);
+        return hipGetLastError();
+    }
     if (nblk > 0) {
-        const size_t lds = (static_cast<size_t>((nh + 1) & ~1)) * sizeof(int32_t) +
-                           kLayoutTokensPerBlock * sizeof(uint64_t);
-        hipLaunchKernelGGL(layout_partial_kernel, dim3(static_cast<unsigned>(nblk)),
+        hipLaunchKernelGGL(layout_partial_kernel<false>, dim3(static_cast<unsigned>(nblk)),
                            dim3(kLayoutTokensPerBlock), lds, stream, topk_idx, T, k, E, R, P,
-                           in_rank, partial);
+                           in_rank, partial, per_expert, per_rank, per_group);
     }
     hipLaunchKernelGGL(layout_reduce_kernel, dim3(static_cast<unsigned>(ceil_div(nh, 256))),
                        dim3(256), 0, stream, partial, static_cast<int>(nblk), E, R, G, per_expert,
