@@ -51,6 +51,7 @@ def _load() -> ctypes.CDLL:
     lib.oracle_dispatch_fp8.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P]
     lib.oracle_combine.argtypes = [P, i64, P, P, i64, i32, i32, P]
     lib.oracle_dispatch_cached.argtypes = [P, P, i64, i32, i32, P, i64]
+    lib.oracle_dispatch_ht.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P]
     lib.oracle_dispatch_fp8_cached.argtypes = [P, P, i64, i32, i32, P, P, i64]
     lib.oracle_quantize_row.argtypes = [P, i32, P, P]
     lib.oracle_e4m3_encode_array.argtypes = [P, i64, P]
@@ -58,7 +59,8 @@ def _load() -> ctypes.CDLL:
     lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3_decode.restype = ctypes.c_float
     for f in ("oracle_layout", "oracle_dispatch", "oracle_dispatch_fp8", "oracle_combine",
-              "oracle_quantize_row", "oracle_dispatch_cached", "oracle_dispatch_fp8_cached"):
+              "oracle_quantize_row", "oracle_dispatch_cached", "oracle_dispatch_fp8_cached",
+              "oracle_dispatch_ht"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -75,7 +77,8 @@ def _use_library(path: Optional[str]) -> None:
         lib = ctypes.CDLL(path)
         for f in ("oracle_layout", "oracle_dispatch", "oracle_dispatch_fp8", "oracle_combine",
                   "oracle_quantize_row", "oracle_e4m3_encode_array", "oracle_bf16_rne_array",
-                  "oracle_e4m3_decode", "oracle_dispatch_cached", "oracle_dispatch_fp8_cached"):
+                  "oracle_e4m3_decode", "oracle_dispatch_cached", "oracle_dispatch_fp8_cached",
+                  "oracle_dispatch_ht"):
             getattr(lib, f).argtypes = getattr(_lib, f).argtypes
             getattr(lib, f).restype = getattr(_lib, f).restype
         _lib = lib
@@ -134,6 +137,29 @@ def dispatch(x: np.ndarray, topk_idx: np.ndarray, topk_weights: Optional[np.ndar
     _check(rc, "oracle_dispatch")
     return dict(recv_x=recv_x, recv_src_idx=src, recv_topk_weights=recv_w,
                 recv_expert_offset=eoff, recv_rank_offset=roff, token_row=trow)
+
+
+def dispatch_ht(x: np.ndarray, topk_idx: np.ndarray, topk_weights: Optional[np.ndarray],
+                num_experts: int, num_ranks: int):
+    """Rank-deduplicated dispatch; receive buffers at capacity T*R rows."""
+    x = _c(x, np.uint16)
+    idx = _c(topk_idx, np.int64)
+    T, k = idx.shape
+    H = x.shape[1]
+    R = num_ranks
+    cap = T * R
+    recv_x = np.zeros((cap, H), np.uint16)
+    src = np.full(cap, -2, np.int32)
+    ridx = np.full((cap, k), -9, np.int64)
+    rw = np.full((cap, k), np.nan, np.float32) if topk_weights is not None else None
+    roff = np.zeros(R + 1, np.int32)
+    trr = np.zeros((T, R), np.int32)
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    rc = _load().oracle_dispatch_ht(_p(x), _p(idx), _p(w), T, H, k, num_experts, R, _p(recv_x),
+                                    _p(src), _p(ridx), _p(rw), _p(roff), _p(trr))
+    _check(rc, "oracle_dispatch_ht")
+    return dict(recv_x=recv_x, recv_src_idx=src, recv_topk_idx=ridx, recv_topk_weights=rw,
+                recv_rank_offset=roff, token_rank_row=trr)
 
 
 def dispatch_fp8(x: np.ndarray, topk_idx: np.ndarray, topk_weights: Optional[np.ndarray],
@@ -196,11 +222,12 @@ def quantize_row(xrow: np.ndarray):
     return q, s[: H // 128]
 
 
-def combine(expert_out: np.ndarray, token_row: np.ndarray, topk_weights: np.ndarray,
+def combine(expert_out: np.ndarray, token_row: np.ndarray, topk_weights: Optional[np.ndarray],
             num_rows: Optional[int] = None):
+    """Weighted gather-sum; topk_weights None means every weight is 1."""
     y = _c(expert_out, np.uint16)
     trow = _c(token_row, np.int32)
-    w = _c(topk_weights, np.float32)
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
     T, k = trow.shape
     H = y.shape[1]
     rows = y.shape[0] if num_rows is None else num_rows

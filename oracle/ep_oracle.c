@@ -351,15 +351,72 @@ int oracle_dispatch_fp8_cached(const uint16_t* x, const int32_t* token_row, int6
     return ORC_OK;
 }
 
+/* High-throughput (rank-deduplicated) dispatch: page "[Not ready] MSCCLPP EP
+ * implementation #852", PR body "Scope / Intranode" (intranode dispatch sends
+ * each token once to every rank that hosts at least one of its experts; the
+ * receiving rank gets the token's top-k ids remapped to its local experts).
+ * One receive row per (t, r) with is_token_in_rank[t, r] = 1, ordered by rank,
+ * then token ascending:
+ *   recv_rank_offset[r]   = first row of rank r, [R] = rows
+ *   token_rank_row[t, r]  = row of (t, r), or -1
+ *   recv_x[row]           = x[t]
+ *   recv_src_idx[row]     = t
+ *   recv_topk_idx[row, j] = topk_idx[t, j] - r*E/R if that expert is on rank r, else -1
+ *   recv_topk_weights[row, j] = topk_weights[t, j] on the same condition, else 0
+ * (The page leaves the weights of non-local slots unspecified; zero is the
+ * reading taken, so a rank can sum its row's weights directly.) */
+int oracle_dispatch_ht(const uint16_t* x, const int64_t* topk_idx, const float* topk_weights,
+                       int64_t T, int H, int k, int E, int R, uint16_t* recv_x,
+                       int32_t* recv_src_idx, int64_t* recv_topk_idx, float* recv_topk_weights,
+                       int32_t* recv_rank_offset, int32_t* token_rank_row)
+{
+    if (!check_routing_args(T, k, E, R) || H < 1) return ORC_EINVAL;
+    if (T * (int64_t)R > INT32_MAX || !recv_rank_offset) return ORC_EINVAL;
+    if (T > 0 && (!x || !topk_idx || !recv_x || !recv_src_idx || !recv_topk_idx || !token_rank_row))
+        return ORC_EINVAL;
+    const int epr = E / R;
+    for (int64_t i = 0; i < T * (int64_t)R; ++i) token_rank_row[i] = 0;
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int64_t e = topk_idx[t * k + j];
+            if (slot_valid(e, E)) token_rank_row[t * R + e / epr] = 1;   /* is_token_in_rank */
+        }
+    for (int r = 0; r <= R; ++r) recv_rank_offset[r] = 0;
+    for (int64_t t = 0; t < T; ++t)
+        for (int r = 0; r < R; ++r) recv_rank_offset[r + 1] += token_rank_row[t * R + r];
+    for (int r = 0; r < R; ++r) recv_rank_offset[r + 1] += recv_rank_offset[r];
+    for (int r = 0; r < R; ++r) {
+        int32_t row = recv_rank_offset[r];
+        for (int64_t t = 0; t < T; ++t) {
+            if (!token_rank_row[t * R + r]) { token_rank_row[t * R + r] = -1; continue; }
+            token_rank_row[t * R + r] = row;
+            recv_src_idx[row] = (int32_t)t;
+            memcpy(recv_x + (int64_t)row * H, x + t * (int64_t)H, sizeof(uint16_t) * (size_t)H);
+            for (int j = 0; j < k; ++j) {
+                int64_t e = topk_idx[t * k + j];
+                int local = slot_valid(e, E) && e / epr == r;
+                recv_topk_idx[(int64_t)row * k + j] = local ? e - (int64_t)r * epr : -1;
+                if (recv_topk_weights)
+                    recv_topk_weights[(int64_t)row * k + j] =
+                        (local && topk_weights) ? topk_weights[t * k + j] : 0.0f;
+            }
+            ++row;
+        }
+    }
+    return ORC_OK;
+}
+
 /* ep_combine: for each token t and channel h, an fp32 accumulator starts at
  * +0 and takes one fused multiply-add per valid slot in fixed top-k (j)
  * order:  acc = fma(w[t,j], y[token_row[t,j], h], acc);  out = bf16_RNE(acc).
- * A slot whose row is negative or >= num_rows contributes nothing. */
+ * A slot whose row is negative or >= num_rows contributes nothing.  Without
+ * weights (NULL) every weight is 1: the plain fp32 sum in j order, which is the
+ * high-throughput combine over a token's per-rank rows (token_rank_row). */
 int oracle_combine(const uint16_t* expert_out, int64_t num_rows, const int32_t* token_row,
                    const float* topk_weights, int64_t T, int H, int k, uint16_t* combined_x)
 {
     if (T < 0 || H < 1 || k < 1 || num_rows < 0) return ORC_EINVAL;
-    if (T > 0 && (!token_row || !topk_weights || !combined_x)) return ORC_EINVAL;
+    if (T > 0 && (!token_row || !combined_x)) return ORC_EINVAL;
     if (T > 0 && num_rows > 0 && !expert_out) return ORC_EINVAL;
     for (int64_t t = 0; t < T; ++t)
         for (int h = 0; h < H; ++h) {
@@ -367,7 +424,8 @@ int oracle_combine(const uint16_t* expert_out, int64_t num_rows, const int32_t* 
             for (int j = 0; j < k; ++j) {
                 int32_t row = token_row[t * k + j];
                 if (row < 0 || (int64_t)row >= num_rows) continue;
-                acc = fmaf(topk_weights[t * k + j], bf16_to_f32(expert_out[(int64_t)row * H + h]), acc);
+                const float wj = topk_weights ? topk_weights[t * k + j] : 1.0f;
+                acc = fmaf(wj, bf16_to_f32(expert_out[(int64_t)row * H + h]), acc);
             }
             combined_x[t * (int64_t)H + h] = oracle_bf16_rne(acc);
         }

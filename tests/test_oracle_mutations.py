@@ -14,6 +14,7 @@ import pytest
 import oracle
 import test_oracle_combine as tc
 import test_oracle_fp8 as tf
+import test_oracle_ht as th
 import test_oracle_layout_rows as tl
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ep_oracle.c")
@@ -38,6 +39,15 @@ def _cached_pins():
     for i in range(len(tl.ROUTINGS)):
         tl.test_cached_dispatch_reproduces_dispatch(i)
     tf.test_fp8_cached_dispatch_matches_fp8_dispatch()
+
+
+def _ht_pins():
+    th.test_hand_worked_example()
+    for i in range(len(tl.ROUTINGS)):
+        th.test_matches_brute_force(i)
+    for name in ("tiny", "large"):
+        th.test_weights_and_slots_conserved(name)
+    th.test_unweighted_combine_closed_form()
 
 
 def _fp8_pins():
@@ -124,6 +134,19 @@ MUTATIONS = {
     "cached_fp8_scale_row": ("recv_scales + (int64_t)row * nb);\n        }\n    return ORC_OK;",
                              "recv_scales + (int64_t)t * nb);\n        }\n    return ORC_OK;",
                              _cached_pins),
+    # rank-deduplicated dispatch
+    "ht_token_major_rows": ("    for (int r = 0; r < R; ++r) {\n        int32_t row = recv_rank_offset[r];\n        for (int64_t t = 0; t < T; ++t) {",
+                            "    for (int r = 0; r < R; ++r) {\n        int32_t row = recv_rank_offset[R - 1 - r];\n        for (int64_t t = 0; t < T; ++t) {",
+                            _ht_pins),
+    "ht_weights_not_masked": ("(local && topk_weights) ? topk_weights[t * k + j] : 0.0f;",
+                              "topk_weights ? topk_weights[t * k + j] : 0.0f;", _ht_pins),
+    "ht_local_by_modulo": ("int local = slot_valid(e, E) && e / epr == r;",
+                           "int local = slot_valid(e, E) && e % R == r;", _ht_pins),
+    "ht_offset_off_by_one": ("for (int64_t t = 0; t < T; ++t)\n        for (int r = 0; r < R; ++r) recv_rank_offset[r + 1] += token_rank_row[t * R + r];",
+                             "for (int64_t t = 1; t < T; ++t)\n        for (int r = 0; r < R; ++r) recv_rank_offset[r + 1] += token_rank_row[t * R + r];",
+                             _ht_pins),
+    "combine_unweighted_zero": ("const float wj = topk_weights ? topk_weights[t * k + j] : 1.0f;",
+                                "const float wj = topk_weights ? topk_weights[t * k + j] : 0.5f;", _ht_pins),
     "bf16_widen_shift": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;", _combine_pins),
 }
 
@@ -147,5 +170,5 @@ def test_planted_mistake_is_caught(name, tmp_path):
 
 
 def test_unmutated_oracle_passes_all_pins():
-    for pins in (_layout_pins, _row_pins, _fp8_pins, _combine_pins, _cached_pins):
+    for pins in (_layout_pins, _row_pins, _fp8_pins, _combine_pins, _cached_pins, _ht_pins):
         pins()
