@@ -116,13 +116,14 @@ MUTATIONS = {
     "combine_drop_last_term": ("for (int j = 0; j < k; ++j) {\n                int32_t row = token_row[t * k + j];\n                if (row < 0 || (int64_t)row >= num_rows) continue;",
                                "for (int j = 0; j < k - 1; ++j) {\n                int32_t row = token_row[t * k + j];\n                if (row < 0 || (int64_t)row >= num_rows) continue;",
                                _combine_pins),
-    "combine_weight_index": ("acc = fmaf(topk_weights[t * k + j],", "acc = fmaf(topk_weights[j],", _combine_pins),
-    "combine_sign": ("acc = fmaf(topk_weights[t * k + j],", "acc = fmaf(-topk_weights[t * k + j],", _combine_pins),
+    "combine_weight_index": ("const float wj = topk_weights ? topk_weights[t * k + j] : 1.0f;",
+                             "const float wj = topk_weights ? topk_weights[j] : 1.0f;", _combine_pins),
+    "combine_sign": ("acc = fmaf(wj,", "acc = fmaf(-wj,", _combine_pins),
     "combine_negzero_start": ("float acc = 0.0f;\n            for (int j = 0; j < k; ++j) {\n                int32_t row",
                               "float acc = -0.0f;\n            for (int j = 0; j < k; ++j) {\n                int32_t row",
                               _combine_pins),
-    "combine_no_range_guard": ("if (row < 0 || (int64_t)row >= num_rows) continue;\n                acc",
-                               "if (row < 0) continue;\n                if (row >= num_rows) row = num_rows - 1;\n                acc",
+    "combine_no_range_guard": ("if (row < 0 || (int64_t)row >= num_rows) continue;\n                const float wj",
+                               "if (row < 0) continue;\n                if (row >= num_rows) row = num_rows - 1;\n                const float wj",
                                _combine_pins),
     # cached dispatch
     "cached_no_range_guard": ("if (row < 0 || (int64_t)row >= num_rows) continue;\n            memcpy(recv_x",
