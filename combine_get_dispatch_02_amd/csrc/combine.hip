@@ -11,6 +11,8 @@
 // acc = fma(w[t,j], y[row(t,j)], acc) in fp32 for j = 0..k-1 in that fixed
 // order (v_fma_f32, one rounding per step), and stores bf16 rounded to
 // nearest even.  The result is therefore independent of the launch shape.
+// Without weights every weight is 1 (fma(1, y, acc) is the rounded sum): the
+// high-throughput combine of a token's per-rank rows.
 #include "ep_device.h"
 #include "ep_launch.h"
 
@@ -38,7 +40,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
         float my_w = 0.0f;
         if (lane < k) {
             my_row = token_row[t * k + lane];
-            my_w = topk_weights[t * k + lane];
+            my_w = topk_weights ? topk_weights[t * k + lane] : 1.0f;
             if (my_row < 0 || static_cast<int64_t>(my_row) >= num_rows) my_row = -1;
         }
         float acc[U][8];

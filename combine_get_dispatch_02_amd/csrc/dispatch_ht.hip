@@ -1,0 +1,175 @@
+// dispatch_ht.hip -- rank-deduplicated ("high-throughput") dispatch on gfx950.
+//
+// Page "[Not ready] MSCCLPP EP implementation #852", PR body "Scope /
+// Intranode": the intranode dispatch sends each token once to every rank that
+// hosts one of its experts, and the receiving rank sees the token's top-k ids
+// remapped to its local experts.  Here the ranks are contiguous ranges of one
+// receive buffer: one row per (token t, rank r) with t routed to r, ordered by
+// rank and then token.
+//
+// Three launches, deterministic, no global atomics:
+//   ht_tile_hist  one token per thread, 256 tokens per tile: the token's rank
+//                 mask (R <= 64) from its k ids; per-tile, per-rank counts
+//   ht_rows       per tile: per-rank prefix over earlier tiles, a 64-lane scan
+//                 over ranks (-> recv_rank_offset), then the rank of each token
+//                 among the tile's tokens routed to the same rank from one
+//                 ballot per rank per wave; writes token_rank_row,
+//                 recv_src_idx and the remapped top-k ids and weights
+//   copy          the bf16 copy kernel of ep_dispatch, driven by the [T, R]
+//                 map token_rank_row instead of the [T, k] token_row
+#include "../../include/ep.h"
+#include "ep_device.h"
+#include "ep_launch.h"
+
+namespace ep {
+namespace {
+
+constexpr int kHtTile = 256;          // tokens per tile = threads per block
+constexpr int kHtWaves = kHtTile / kWave;
+constexpr int kHtHistBatch = 64;
+
+__device__ __forceinline__ uint64_t rank_mask(const int64_t* __restrict__ ids, int k, int E, int epr) {
+    uint64_t m = 0;
+    for (int j = 0; j < k; ++j) {
+        const int64_t e = ids[j];
+        if (e >= 0 && e < E) m |= uint64_t(1) << static_cast<int>(e / epr);
+    }
+    return m;
+}
+
+__global__ __launch_bounds__(kHtTile) void ht_tile_hist_kernel(const int64_t* __restrict__ topk_idx,
+                                                              int64_t T, int k, int E, int R,
+                                                              int32_t* __restrict__ hist) {
+    __shared__ int32_t h[EP_MAX_RANKS];
+    if (threadIdx.x < R) h[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kHtTile + threadIdx.x;
+    if (t < T) {
+        for (uint64_t b = rank_mask(topk_idx + t * k, k, E, E / R); b; b &= b - 1)
+            atomicAdd(&h[__builtin_ctzll(b)], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x < R) hist[static_cast<int64_t>(blockIdx.x) * R + threadIdx.x] = h[threadIdx.x];
+}
+
+__global__ __launch_bounds__(kHtTile) void ht_rows_kernel(
+    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int64_t T,
+    int k, int E, int R, int ntiles, const int32_t* __restrict__ hist,
+    int32_t* __restrict__ token_rank_row, int32_t* __restrict__ recv_src_idx,
+    int64_t* __restrict__ recv_topk_idx, float* __restrict__ recv_w,
+    int32_t* __restrict__ rank_offset) {
+    __shared__ int32_t base[EP_MAX_RANKS];                 // first row of rank r for this tile
+    __shared__ int32_t wcnt[kHtWaves][EP_MAX_RANKS];       // per-wave counts -> offsets
+    const int c = blockIdx.x;
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int epr = E / R;
+    const int64_t t = static_cast<int64_t>(c) * kHtTile + threadIdx.x;
+    const bool in = t < T;
+    // This token's mask (its ids are loaded here; they and the weights are
+    // read again, from L2, when the rows are written).
+    const uint64_t m = in ? rank_mask(topk_idx + t * k, k, E, epr) : 0;
+
+    // Per rank: tokens in all tiles and in the tiles before this one.
+    if (threadIdx.x < kWave) {
+        const int r = lane;
+        int tot = 0, pre = 0;
+        if (r < R) {
+            for (int c0 = 0; c0 < ntiles; c0 += kHtHistBatch) {
+                int v[kHtHistBatch];
+#pragma unroll
+                for (int i = 0; i < kHtHistBatch; ++i)
+                    v[i] = (c0 + i < ntiles) ? hist[static_cast<int64_t>(c0 + i) * R + r] : 0;
+#pragma unroll
+                for (int i = 0; i < kHtHistBatch; ++i) {
+                    tot += v[i];
+                    pre += (c0 + i < c) ? v[i] : 0;
+                }
+            }
+        }
+        // exclusive scan of the totals over ranks (one lane per rank)
+        int incl = tot;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int u = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += u;
+        }
+        const int excl = incl - tot;
+        if (r < R) base[r] = excl + pre;
+        if (c == 0) {
+            if (r < R) rank_offset[r] = excl;
+            if (r == R - 1) rank_offset[R] = incl;
+        }
+    }
+    // In-tile ranks: one ballot per rank per wave.
+    for (int r = 0; r < R; ++r) {
+        const uint64_t b = ballot((m >> r) & 1);
+        if (lane == 0) wcnt[wave][r] = __popcll(b);
+    }
+    __syncthreads();
+    if (threadIdx.x < R) {
+        int run = base[threadIdx.x];
+        for (int w = 0; w < kHtWaves; ++w) {
+            const int v = wcnt[w][threadIdx.x];
+            wcnt[w][threadIdx.x] = run;
+            run += v;
+        }
+    }
+    __syncthreads();
+    if (!in) return;
+    // Lanes past the last token have m == 0, so they add nothing to a ballot
+    // whether or not they take part in it.
+    const int64_t* ids = topk_idx + t * k;
+    for (int r = 0; r < R; ++r) {
+        const uint64_t b = ballot((m >> r) & 1);
+        int row = -1;
+        if ((m >> r) & 1) row = wcnt[wave][r] + __popcll(b & lanes_below());
+        token_rank_row[t * R + r] = row;
+        if (row >= 0) {
+            recv_src_idx[row] = static_cast<int32_t>(t);
+            for (int j = 0; j < k; ++j) {
+                const int64_t e = ids[j];
+                const bool local = e >= 0 && e < E && e / epr == r;
+                recv_topk_idx[static_cast<int64_t>(row) * k + j] =
+                    local ? e - static_cast<int64_t>(r) * epr : -1;
+                if (recv_w)
+                    recv_w[static_cast<int64_t>(row) * k + j] =
+                        (local && topk_weights) ? topk_weights[t * k + j] : 0.0f;
+            }
+        }
+    }
+}
+
+__global__ void ht_zero_offsets_kernel(int32_t* rank_offset, int R) {
+    if (static_cast<int>(threadIdx.x) <= R) rank_offset[threadIdx.x] = 0;
+}
+
+}  // namespace
+
+size_t ht_workspace_bytes(int64_t T, int R) {
+    const size_t b = static_cast<size_t>(ceil_div(T, kHtTile)) * static_cast<size_t>(R) * sizeof(int32_t);
+    return round_up(b > 0 ? b : 1, 256);
+}
+
+hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                              int64_t T, int H, int k, int E, int R, void* recv_x,
+                              int32_t* recv_src_idx, int64_t* recv_topk_idx, float* recv_w,
+                              int32_t* rank_offset, int32_t* token_rank_row, void* workspace,
+                              hipStream_t stream) {
+    if (T == 0) {
+        hipLaunchKernelGGL(ht_zero_offsets_kernel, dim3(1), dim3(2 * kWave), 0, stream, rank_offset, R);
+        return hipGetLastError();
+    }
+    const int ntiles = static_cast<int>(ceil_div(T, kHtTile));
+    int32_t* hist = static_cast<int32_t*>(workspace);
+    hipLaunchKernelGGL(ht_tile_hist_kernel, dim3(ntiles), dim3(kHtTile), 0, stream, topk_idx, T, k,
+                       E, R, hist);
+    hipLaunchKernelGGL(ht_rows_kernel, dim3(ntiles), dim3(kHtTile), 0, stream, topk_idx,
+                       (recv_w ? topk_weights : nullptr), T, k, E, R, ntiles, hist, token_rank_row,
+                       recv_src_idx, recv_topk_idx, recv_w, rank_offset);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_dispatch_copy_bf16(x, token_rank_row, recv_x, T * R, T, H, R, stream);
+}
+
+}  // namespace ep

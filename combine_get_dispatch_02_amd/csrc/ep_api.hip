@@ -228,6 +228,38 @@ int ep_dispatch_fp8_cached(const void* x, const int32_t* token_row, int64_t num_
                       fn);
 }
 
+size_t ep_dispatch_ht_workspace_bytes(int64_t num_tokens, int num_ranks) {
+    if (num_tokens < 0 || num_ranks < 1) return 0;
+    return ep::ht_workspace_bytes(num_tokens, num_ranks);
+}
+
+int ep_dispatch_ht(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                   int64_t num_tokens, int hidden, int num_topk, int num_experts, int num_ranks,
+                   void* recv_x, int32_t* recv_src_idx, int64_t* recv_topk_idx,
+                   float* recv_topk_weights, int32_t* recv_rank_offset, int32_t* token_rank_row,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "ep_dispatch_ht";
+    int s = check_routing(fn, topk_idx, num_tokens, num_topk, num_experts, num_ranks);
+    if (s != EP_OK) return s;
+    if (hidden < 8 || hidden % 8 != 0)
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: hidden must be a positive multiple of 8", fn);
+    if (num_tokens * static_cast<int64_t>(num_ranks) > INT32_MAX)
+        return fail(EP_ERR_UNSUPPORTED, "%s: num_tokens * num_ranks >= 2^31", fn);
+    if (!recv_rank_offset) return fail(EP_ERR_INVALID_ARGUMENT, "%s: recv_rank_offset is NULL", fn);
+    if (num_tokens > 0 && (!x || !recv_x || !recv_src_idx || !recv_topk_idx || !token_rank_row))
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: a required pointer is NULL", fn);
+    if (num_tokens > 0 && (!aligned16(x) || !aligned16(recv_x)))
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: x and recv_x must be 16-byte aligned", fn);
+    const size_t need = ep::ht_workspace_bytes(num_tokens, num_ranks);
+    if (num_tokens > 0 && (!workspace || workspace_bytes < need))
+        return fail(EP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes", fn, need);
+    return hip_status(ep::launch_dispatch_ht(x, topk_idx, topk_weights, num_tokens, hidden, num_topk,
+                                             num_experts, num_ranks, recv_x, recv_src_idx,
+                                             recv_topk_idx, recv_topk_weights, recv_rank_offset,
+                                             token_rank_row, workspace, static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
 int ep_combine(const void* expert_out, int64_t num_rows, const int32_t* token_row,
                const float* topk_weights, int64_t num_tokens, int hidden, int num_topk,
                void* combined_x, void* stream) {
@@ -238,7 +270,7 @@ int ep_combine(const void* expert_out, int64_t num_rows, const int32_t* token_ro
     if (num_topk > EP_MAX_TOPK) return fail(EP_ERR_UNSUPPORTED, "%s: num_topk > %d", fn, EP_MAX_TOPK);
     if (hidden < 8 || hidden % 8 != 0)
         return fail(EP_ERR_INVALID_ARGUMENT, "%s: hidden must be a positive multiple of 8", fn);
-    if (num_tokens > 0 && (!token_row || !topk_weights || !combined_x))
+    if (num_tokens > 0 && (!token_row || !combined_x))
         return fail(EP_ERR_INVALID_ARGUMENT, "%s: a required pointer is NULL", fn);
     if (num_tokens > 0 && num_rows > 0 && !expert_out)
         return fail(EP_ERR_INVALID_ARGUMENT, "%s: expert_out is NULL", fn);

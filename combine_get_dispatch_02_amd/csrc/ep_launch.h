@@ -56,6 +56,14 @@ hipError_t launch_dispatch_small_fp8(const void* x, const int64_t* topk_idx,
                                      int32_t* expert_offset, int32_t* rank_offset,
                                      int32_t* token_row, hipStream_t stream);
 
+// ---- rank-deduplicated (high-throughput) dispatch -------------------------------
+size_t ht_workspace_bytes(int64_t T, int R);
+hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                              int64_t T, int H, int k, int E, int R, void* recv_x,
+                              int32_t* recv_src_idx, int64_t* recv_topk_idx, float* recv_w,
+                              int32_t* rank_offset, int32_t* token_rank_row, void* workspace,
+                              hipStream_t stream);
+
 // ---- data movement ------------------------------------------------------------
 // Copy kernels: every slot whose row lies in [0, num_rows) receives x[t]
 // (bf16) or its FP8 cast; other slots are skipped.

@@ -53,9 +53,12 @@ def lib() -> ctypes.CDLL:
     L.ep_dispatch_fp8.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, sz, P]
     L.ep_combine.argtypes = [P, i64, P, P, i64, i32, i32, P, P]
     L.ep_dispatch_cached.argtypes = [P, P, i64, i32, i32, P, i64, P]
+    L.ep_dispatch_ht_workspace_bytes.argtypes = [i64, i32]
+    L.ep_dispatch_ht_workspace_bytes.restype = sz
+    L.ep_dispatch_ht.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, sz, P]
     L.ep_dispatch_fp8_cached.argtypes = [P, P, i64, i32, i32, P, P, i64, P]
     for f in ("ep_get_dispatch_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_combine",
-              "ep_dispatch_cached", "ep_dispatch_fp8_cached"):
+              "ep_dispatch_cached", "ep_dispatch_fp8_cached", "ep_dispatch_ht"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -253,21 +256,67 @@ def ep_dispatch_fp8_cached(x: torch.Tensor, token_row: torch.Tensor, recv_rows: 
     return out
 
 
-def ep_combine(expert_out: torch.Tensor, token_row: torch.Tensor, topk_weights: torch.Tensor,
-               num_rows: Optional[int] = None, *, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+def ep_dispatch_ht_workspace_bytes(num_tokens: int, num_ranks: int) -> int:
+    return int(lib().ep_dispatch_ht_workspace_bytes(num_tokens, num_ranks))
+
+
+def ep_dispatch_ht(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: Optional[torch.Tensor],
+                   num_experts: int, num_ranks: int, *,
+                   out: Optional[Dict[str, torch.Tensor]] = None,
+                   workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Rank-deduplicated dispatch: recv_x [T*R, H] (recv_rank_offset[R] rows
+    filled), recv_src_idx, recv_topk_idx [T*R, k] int64 (local ids, -1
+    elsewhere), recv_topk_weights [T*R, k], recv_rank_offset [R+1] and
+    token_rank_row [T, R]; combine with ep_combine(y, token_rank_row, None)."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    _need(topk_idx, "topk_idx", torch.int64, dev)
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32, dev)
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    R = num_ranks
+    if topk_idx.shape[0] != T:
+        raise ValueError("x and topk_idx disagree on num_tokens")
+    if out is None:
+        cap = T * R
+        out = dict(recv_x=torch.empty((cap, H), dtype=torch.bfloat16, device=dev),
+                   recv_src_idx=torch.empty(cap, dtype=torch.int32, device=dev),
+                   recv_topk_idx=torch.empty((cap, k), dtype=torch.int64, device=dev),
+                   recv_topk_weights=(torch.empty((cap, k), dtype=torch.float32, device=dev)
+                                      if topk_weights is not None else None),
+                   recv_rank_offset=torch.empty(R + 1, dtype=torch.int32, device=dev),
+                   token_rank_row=torch.empty((T, R), dtype=torch.int32, device=dev))
+    ws = _workspace(ep_dispatch_ht_workspace_bytes(T, R), dev, workspace)
+    with torch.cuda.device(dev):
+        st = lib().ep_dispatch_ht(
+            _ptr(x), _ptr(topk_idx), _ptr(topk_weights), T, H, k, num_experts, R,
+            _ptr(out["recv_x"]), _ptr(out["recv_src_idx"]), _ptr(out["recv_topk_idx"]),
+            _ptr(out.get("recv_topk_weights")), _ptr(out["recv_rank_offset"]),
+            _ptr(out["token_rank_row"]), _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "ep_dispatch_ht")
+    return out
+
+
+def ep_combine(expert_out: torch.Tensor, token_row: torch.Tensor,
+               topk_weights: Optional[torch.Tensor], num_rows: Optional[int] = None, *,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Weighted top-k gather-sum: combined_x [T, H] bf16.  num_rows defaults to
-    expert_out.shape[0]; slots whose row is outside [0, num_rows) are skipped."""
+    expert_out.shape[0]; slots whose row is outside [0, num_rows) are skipped.
+    topk_weights None: every weight is 1 (the combine of ep_dispatch_ht's
+    per-rank rows, with token_rank_row as the map)."""
     _need(expert_out, "expert_out", torch.bfloat16)
     dev = expert_out.device
     _need(token_row, "token_row", torch.int32, dev)
-    _need(topk_weights, "topk_weights", torch.float32, dev)
     T, k = token_row.shape
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32, dev)
+        if tuple(topk_weights.shape) != (T, k):
+            raise ValueError("topk_weights must have the shape of token_row")
     H = expert_out.shape[1]
     rows = expert_out.shape[0] if num_rows is None else int(num_rows)
     if rows > expert_out.shape[0]:
         raise ValueError("num_rows exceeds expert_out rows")
-    if tuple(topk_weights.shape) != (T, k):
-        raise ValueError("topk_weights must have the shape of token_row")
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     with torch.cuda.device(dev):

@@ -187,17 +187,51 @@ int ep_dispatch_fp8_cached(const void* x, const int32_t* token_row, int64_t num_
                            int64_t recv_rows, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * ep_dispatch_ht -- rank-deduplicated ("high-throughput") dispatch: the
+ * intranode dispatch of page #852, "Scope / Intranode", which sends each
+ * token once to every rank hosting at least one of its experts, the receiver
+ * seeing the token's top-k ids remapped to its local experts.  One receive
+ * row per (token t, rank r) with t routed to r (is_token_in_rank[t, r] = 1),
+ * ordered by rank, then token:
+ *
+ *   recv_x            [T*R, H]  bf16  out: row = x[t], bit for bit (capacity
+ *                                     T*R rows; recv_rank_offset[R] filled)
+ *   recv_src_idx      [T*R]     int32 out: source token of each filled row
+ *   recv_topk_idx     [T*R, k]  int64 out: topk_idx[t, j] - r*E/R when that
+ *                                     expert is on rank r, else -1
+ *   recv_topk_weights [T*R, k]  fp32  out: topk_weights[t, j] on the same
+ *                                     condition, else 0 (may be NULL)
+ *   recv_rank_offset  [R+1]     int32 out: first row of each rank; [R] = rows
+ *   token_rank_row    [T, R]    int32 out: row of (t, r), or -1
+ *
+ * The matching combine is ep_combine(expert_out, rows, token_rank_row, NULL,
+ * T, H, R, out): out[t] = bf16(sum over ranks, in rank order, of the rank's
+ * row for t), each row holding that rank's already weighted partial result.
+ * Requires H % 8 == 0, T*R < 2^31 and the routing limits above.
+ * Workspace: ep_dispatch_ht_workspace_bytes(T, R).
+ * ------------------------------------------------------------------------- */
+size_t ep_dispatch_ht_workspace_bytes(int64_t num_tokens, int num_ranks);
+
+int ep_dispatch_ht(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                   int64_t num_tokens, int hidden, int num_topk, int num_experts, int num_ranks,
+                   void* recv_x, int32_t* recv_src_idx, int64_t* recv_topk_idx,
+                   float* recv_topk_weights, int32_t* recv_rank_offset, int32_t* token_rank_row,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * ep_combine -- gather each token's expert outputs back and sum them weighted
  * by topk_weights (intranode combine of "Scope / Intranode", consuming the
  * receiver-side map token_row that dispatch produced).  For every t, h:
  *   acc = +0.0f;  for j = 0 .. k-1 in this order, if 0 <= token_row[t,j] < num_rows:
  *       acc = fmaf(topk_weights[t,j], expert_out[token_row[t,j], h], acc);
  *   combined_x[t, h] = bf16(acc), rounded to nearest even.
+ * topk_weights may be NULL: every weight is then 1 (a plain fp32 sum in j
+ * order), which is the combine of ep_dispatch_ht's per-rank rows.
  *
  *   expert_out   [num_rows, H] bf16 in (16-byte aligned)
  *   token_row    [T, k]        int32 in (from ep_dispatch; rows outside
  *                              [0, num_rows) are skipped, never read)
- *   topk_weights [T, k]        fp32  in
+ *   topk_weights [T, k]        fp32  in (NULL: all weights 1)
  *   combined_x   [T, H]        bf16  out (16-byte aligned)
  * Requires H % 8 == 0, 1 <= k <= EP_MAX_TOPK, num_rows >= 0.  No workspace.
  * ------------------------------------------------------------------------- */

@@ -99,7 +99,7 @@ def test_dispatch_fp8_specific_rejects(kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(T=-1), EINVAL), (dict(rows=-1), EINVAL), (dict(k=0), EINVAL), (dict(k=65), EUNSUP),
-    (dict(H=4), EINVAL), (dict(H=20), EINVAL), (dict(trow=None), EINVAL), (dict(w=None), EINVAL),
+    (dict(H=4), EINVAL), (dict(H=20), EINVAL), (dict(trow=None), EINVAL),
     (dict(out=None), EINVAL), (dict(y=None), EINVAL), (dict(out=ctypes.c_void_p(0x100002)), EINVAL),
     (dict(y=ctypes.c_void_p(0x100008)), EINVAL),
 ])
@@ -144,3 +144,28 @@ def test_fp8_cached_specific_rejects(kw):
     st = ep.lib().ep_dispatch_fp8_cached(a["x"], a["trow"], a["T"], a["H"], a["k"], a["recv"],
                                          a["scales"], a["rows"], None)
     assert st == EINVAL
+
+
+def _ht(**kw):
+    a = dict(x=FAKE, idx=FAKE, w=None, T=16, H=256, k=2, E=8, R=4, recv=FAKE, src=FAKE, ridx=FAKE,
+             rw=None, roff=FAKE, trr=FAKE, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return ep.lib().ep_dispatch_ht(a["x"], a["idx"], a["w"], a["T"], a["H"], a["k"], a["E"], a["R"],
+                                   a["recv"], a["src"], a["ridx"], a["rw"], a["roff"], a["trr"],
+                                   a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), EINVAL), (dict(k=0), EINVAL), (dict(k=65), EUNSUP), (dict(E=9), EINVAL),
+    (dict(R=65, E=130), EUNSUP), (dict(H=12), EINVAL), (dict(x=None), EINVAL), (dict(recv=None), EINVAL),
+    (dict(src=None), EINVAL), (dict(ridx=None), EINVAL), (dict(roff=None), EINVAL), (dict(trr=None), EINVAL),
+    (dict(x=ctypes.c_void_p(0x100008)), EINVAL), (dict(wsb=4), EWS), (dict(ws=None), EWS),
+    (dict(T=2 ** 26, R=64, E=64, k=8), EUNSUP),
+])
+def test_dispatch_ht_rejects(kw, code):
+    assert _ht(**kw) == code
+
+
+def test_ht_workspace_size():
+    assert ep.ep_dispatch_ht_workspace_bytes(4096, 8) >= 16 * 8 * 4
+    assert ep.ep_dispatch_ht_workspace_bytes(-1, 8) == 0
