@@ -4,7 +4,9 @@
 One step is one pass of the whole hot path over one batch of synthetic
 input already resident in HBM:
     ep_get_dispatch_layout -> ep_dispatch -> ep_combine -> ep_dispatch_fp8
-with the combine fed the dispatched rows (identity experts).  Before each
+with the combine fed the dispatched rows (identity experts), followed by the
+rank-deduplicated pair ep_dispatch_ht -> ep_combine (unweighted, over the
+per-rank rows), reported as extra phases beside the headline.  Before each
 phase (outside its events) a 512 MiB write followed by a 512 MiB read of
 another buffer evicts L2 and the 256 MB Infinity Cache: the phase's inputs
 are then only in HBM and the caches hold clean, unrelated lines, so no
@@ -49,10 +51,22 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(wl):
+def ht_rows(wl, idx):
+    """Rows of the rank-deduplicated dispatch: one per (token, rank it reaches)."""
+    import numpy as np
+    valid = (idx >= 0) & (idx < wl.E)
+    hit = np.zeros((wl.T, wl.R), dtype=bool)
+    t, j = np.nonzero(valid)
+    hit[t, idx[t, j] // (wl.E // wl.R)] = True
+    return int(hit.sum())
+
+
+def algorithmic_bytes(wl, n_ht=None):
     """Bytes each call must move at least (read once, write once)."""
     T, H, k, E, R, G = wl.T, wl.H, wl.k, wl.E, wl.R, wl.G
     N = T * k
+    n = T * R if n_ht is None else n_ht
+    ht_maps = 4 * T * R + 4 * n + 8 * n * k + 4 * n * k + 4 * (R + 1)   # token_rank_row, src, ids, w
     maps = 4 * N + 4 * N + 4 * T * k + 4 * (E + 1) + 4 * (R + 1)   # src, recv_w, token_row, offsets
     reads = 8 * T * k + 4 * T * k                                  # topk_idx, topk_weights
     return dict(
@@ -60,6 +74,8 @@ def algorithmic_bytes(wl):
         dispatch=reads + 2 * T * H + 2 * N * H + maps,
         dispatch_fp8=reads + 2 * T * H + N * H + 4 * N * (H // 128) + maps,
         combine=4 * T * k + 4 * T * k + 2 * N * H + 2 * T * H,
+        dispatch_ht=8 * T * k + 4 * T * k + 2 * T * H + 2 * n * H + ht_maps,
+        combine_ht=4 * T * R + 2 * n * H + 2 * T * H,
     )
 
 
@@ -241,10 +257,20 @@ def main():
     fp8["recv_scales"] = torch.empty((N, H // 128), dtype=torch.float32, device=dev)
     ws_d = torch.empty(ep.ep_dispatch_workspace_bytes(T, k, E), dtype=torch.uint8, device=dev)
     comb = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    cap_ht = T * R
+    ht = dict(recv_x=torch.empty((cap_ht, H), dtype=torch.bfloat16, device=dev),
+              recv_src_idx=torch.empty(cap_ht, dtype=torch.int32, device=dev),
+              recv_topk_idx=torch.empty((cap_ht, k), dtype=torch.int64, device=dev),
+              recv_topk_weights=torch.empty((cap_ht, k), dtype=torch.float32, device=dev),
+              recv_rank_offset=torch.empty(R + 1, dtype=torch.int32, device=dev),
+              token_rank_row=torch.empty((T, R), dtype=torch.int32, device=dev))
+    ws_ht = torch.empty(ep.ep_dispatch_ht_workspace_bytes(T, R), dtype=torch.uint8, device=dev)
+    comb_ht = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    n_ht = ht_rows(wl, idx)
     flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     flush_src = torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
 
-    phases = ["layout", "dispatch", "combine", "dispatch_fp8"]
+    phases = ["layout", "dispatch", "combine", "dispatch_fp8", "dispatch_ht", "combine_ht"]
 
     def flush(i):
         if not args.no_flush:
@@ -266,9 +292,17 @@ def main():
         ev[5].record()
         ep.ep_dispatch_fp8(xd, idxd, wd, E, R, out=fp8, workspace=ws_d)
         ev[6].record()
+        flush(i + 3)
+        ev[7].record()
+        ep.ep_dispatch_ht(xd, idxd, wd, E, R, out=ht, workspace=ws_ht)
+        ev[8].record()
+        flush(i + 4)
+        ev[9].record()
+        ep.ep_combine(ht["recv_x"], ht["token_rank_row"], None, num_rows=n_ht, out=comb_ht)
+        ev[10].record()
 
     def events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+        return [torch.cuda.Event(enable_timing=True) for _ in range(11)]
 
     if args.graph:
         graph_mode(args, wl, ep, torch, np, idxd, xd, wd, lay, ws_l, disp, ws_d, comb, fp8)
@@ -279,6 +313,8 @@ def main():
     torch.cuda.synchronize()
     if disp["recv_expert_offset"][-1].item() != N:
         raise RuntimeError("dispatch filled an unexpected number of rows")
+    if ht["recv_rank_offset"][-1].item() != n_ht:
+        raise RuntimeError("rank-deduplicated dispatch filled an unexpected number of rows")
 
     evs = [events() for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -297,11 +333,13 @@ def main():
         torch.cuda.synchronize()
 
     ms = {p: np.array([e[a].elapsed_time(e[b]) for e in evs])
-          for p, (a, b) in zip(phases, [(0, 1), (1, 2), (3, 4), (5, 6)])}
-    B = algorithmic_bytes(wl)
+          for p, (a, b) in zip(phases, [(0, 1), (1, 2), (3, 4), (5, 6), (7, 8), (9, 10)])}
+    B = algorithmic_bytes(wl, n_ht)
     t_dc = float(ms["dispatch"].sum() + ms["combine"].sum()) / 1e3
     value = (B["dispatch"] + B["combine"]) * args.steps / t_dc / 1e9
-    step_ms = float(sum(ms[p].mean() for p in phases))
+    step_ms = float(sum(ms[p].mean() for p in phases[:4]))
+    t_ht = float(ms["dispatch_ht"].sum() + ms["combine_ht"].sum()) / 1e3
+    ht_gbs = (B["dispatch_ht"] + B["combine_ht"]) * args.steps / t_ht / 1e9
     phase_info = {}
     for p in phases:
         us = ms[p] * 1e3
@@ -343,6 +381,11 @@ def main():
         "caches_flushed_between_phases": not args.no_flush,
         "wall_ms_per_step_incl_flush": round(1e3 * wall / args.steps, 4),
         "phases": phase_info,
+        "rank_dedup": {"rows": n_ht, "rows_per_token": round(n_ht / max(T, 1), 4),
+                       "dispatch_plus_combine_GBps": round(ht_gbs, 1),
+                       "pct_of_hbm_peak": round(100 * ht_gbs / HBM_PEAK_GBS, 2),
+                       "us_per_pair": round(1e6 * t_ht / args.steps, 2),
+                       "note": "ep_dispatch_ht + unweighted ep_combine; not part of value or ms_per_step"},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -11,8 +11,9 @@
 // acc = fma(w[t,j], y[row(t,j)], acc) in fp32 for j = 0..k-1 in that fixed
 // order (v_fma_f32, one rounding per step), and stores bf16 rounded to
 // nearest even.  The result is therefore independent of the launch shape.
-// Without weights every weight is 1 (fma(1, y, acc) is the rounded sum): the
-// high-throughput combine of a token's per-rank rows.
+// Without weights every weight is 1: the high-throughput combine of a token's
+// per-rank rows.  That case has its own instantiation, which loads no weights
+// and adds (acc + y rounds exactly as fma(1, y, acc) does).
 #include "ep_device.h"
 #include "ep_launch.h"
 
@@ -24,7 +25,7 @@ __device__ __forceinline__ int64_t wave_index() {
            __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
 }
 
-template <int U, int KB>
+template <int U, int KB, bool kWeighted>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ y,
                                                       int64_t num_rows,
                                                       const int32_t* __restrict__ token_row,
@@ -40,7 +41,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
         float my_w = 0.0f;
         if (lane < k) {
             my_row = token_row[t * k + lane];
-            my_w = topk_weights ? topk_weights[t * k + lane] : 1.0f;
+            if (kWeighted) my_w = topk_weights[t * k + lane];
             if (my_row < 0 || static_cast<int64_t>(my_row) >= num_rows) my_row = -1;
         }
         float acc[U][8];
@@ -68,14 +69,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
 #pragma unroll
             for (int jj = 0; jj < KB; ++jj) {
                 if (rows[jj] < 0) continue;
-                const float wj = read_lane(my_w, j0 + jj);
+                if (kWeighted) {
+                    const float wj = read_lane(my_w, j0 + jj);
 #pragma unroll
-                for (int u = 0; u < U; ++u)
+                    for (int u = 0; u < U; ++u)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[u][2 * i] = __builtin_fmaf(wj, bf16_lo(val[jj][u][i]), acc[u][2 * i]);
-                        acc[u][2 * i + 1] = __builtin_fmaf(wj, bf16_hi(val[jj][u][i]), acc[u][2 * i + 1]);
-                    }
+                        for (int i = 0; i < 4; ++i) {
+                            acc[u][2 * i] = __builtin_fmaf(wj, bf16_lo(val[jj][u][i]), acc[u][2 * i]);
+                            acc[u][2 * i + 1] = __builtin_fmaf(wj, bf16_hi(val[jj][u][i]), acc[u][2 * i + 1]);
+                        }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            acc[u][2 * i] += bf16_lo(val[jj][u][i]);
+                            acc[u][2 * i + 1] += bf16_hi(val[jj][u][i]);
+                        }
+                }
             }
         }
         u32x4* dst = out + t * V;
@@ -93,14 +104,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
     }
 }
 
-template <int U, int KB>
+template <int U, int KB, bool kWeighted>
 hipError_t launch_u(const void* y, int64_t num_rows, const int32_t* token_row, const float* w,
                     void* out, int64_t T, int V, int k, hipStream_t stream) {
     const int tiles_per_token = static_cast<int>(ceil_div(V, U * kWave));
     const int64_t num_tiles = T * tiles_per_token;
     const int64_t blocks = ceil_div(num_tiles, 4);
-    const unsigned grid = static_cast<unsigned>(blocks < (1 << 30) ? blocks : (1 << 30));
-    hipLaunchKernelGGL((combine_kernel<U, KB>), dim3(grid), dim3(256), 0, stream,
+    const int64_t cap = kMaxLaunchThreads / 256;
+    const unsigned grid = static_cast<unsigned>(blocks < cap ? blocks : cap);
+    hipLaunchKernelGGL((combine_kernel<U, KB, kWeighted>), dim3(grid), dim3(256), 0, stream,
                        static_cast<const u32x4*>(y), num_rows, token_row, w,
                        static_cast<u32x4*>(out), V, k, tiles_per_token, num_tiles);
     return hipGetLastError();
@@ -113,9 +125,12 @@ hipError_t launch_combine(const void* expert_out, int64_t num_rows, const int32_
                           hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
-    if (V % (2 * kWave) == 0 && T * (V / (2 * kWave)) >= 4096)
-        return launch_u<2, 8>(expert_out, num_rows, token_row, topk_weights, out, T, V, k, stream);
-    return launch_u<1, 8>(expert_out, num_rows, token_row, topk_weights, out, T, V, k, stream);
+    const bool wide = V % (2 * kWave) == 0 && T * (V / (2 * kWave)) >= 4096;
+    if (topk_weights)
+        return wide ? launch_u<2, 8, true>(expert_out, num_rows, token_row, topk_weights, out, T, V, k, stream)
+                    : launch_u<1, 8, true>(expert_out, num_rows, token_row, topk_weights, out, T, V, k, stream);
+    return wide ? launch_u<2, 8, false>(expert_out, num_rows, token_row, nullptr, out, T, V, k, stream)
+                : launch_u<1, 8, false>(expert_out, num_rows, token_row, nullptr, out, T, V, k, stream);
 }
 
 }  // namespace ep

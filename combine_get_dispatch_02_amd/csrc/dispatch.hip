@@ -354,8 +354,7 @@ __device__ __forceinline__ int64_t wave_index() {
 // it once; each lane then issues kCopyVec 16-byte non-temporal stores per
 // row.  On MI355X this drains a 1:k fan-out faster than one wave storing one
 // load to all k rows (measured: ~6% at 4096 x 7168, k = 8); longer runs per
-// wave (4 or 7 vectors per lane) were markedly slower.
-constexpr int kCopyVec = 2;
+// wave (4 or 7 vectors per lane) were markedly slower.  (kCopyVec = 2.)
 
 __global__ __launch_bounds__(512) void copy_bf16_kernel(const u32x4* __restrict__ x,
                                                         const int32_t* __restrict__ token_row,
@@ -683,6 +682,12 @@ static size_t small_lds_bytes(int E) {
 
 bool dispatch_is_small(int64_t T, int k) { return T > 0 && T * k <= kSmallSlots; }
 
+bool copy_launch_fits(int64_t T, int H, int fanout) {
+    const int64_t segs = ceil_div(H / 8, kCopyVec * kWave);
+    const int64_t kb = fanout < 8 ? fanout : 8;
+    return T * segs * kb * kWave <= kMaxLaunchThreads;
+}
+
 hipError_t launch_dispatch_small_bf16(const void* x, const int64_t* topk_idx,
                                       const float* topk_weights, int64_t T, int H, int k, int E,
                                       int R, void* recv_x, int32_t* recv_src_idx, float* recv_w,
@@ -734,7 +739,8 @@ hipError_t launch_dispatch_copy_fp8(const void* x, const int32_t* token_row, uin
     const int tiles_per_token = static_cast<int>(ceil_div(H, 1024));
     const int64_t num_tiles = T * tiles_per_token;
     const int64_t blocks = ceil_div(num_tiles, 4);
-    const unsigned grid = static_cast<unsigned>(blocks < (1 << 30) ? blocks : (1 << 30));
+    const int64_t cap = kMaxLaunchThreads / 256;
+    const unsigned grid = static_cast<unsigned>(blocks < cap ? blocks : cap);
     hipLaunchKernelGGL(copy_fp8_kernel, dim3(grid), dim3(256), 0, stream,
                        static_cast<const u32x4*>(x), token_row, recv_q, recv_scales, num_rows, H, k,
                        tiles_per_token, num_tiles);

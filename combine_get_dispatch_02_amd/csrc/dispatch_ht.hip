@@ -7,14 +7,17 @@
 // receive buffer: one row per (token t, rank r) with t routed to r, ordered by
 // rank and then token.
 //
-// Three launches, deterministic, no global atomics:
+// Four launches, deterministic, no global atomics:
 //   ht_tile_hist  one token per thread, 256 tokens per tile: the token's rank
 //                 mask (R <= 64) from its k ids; per-tile, per-rank counts
 //   ht_rows       per tile: per-rank prefix over earlier tiles, a 64-lane scan
 //                 over ranks (-> recv_rank_offset), then the rank of each token
 //                 among the tile's tokens routed to the same rank from one
-//                 ballot per rank per wave; writes token_rank_row,
-//                 recv_src_idx and the remapped top-k ids and weights
+//                 ballot per rank per wave; writes token_rank_row
+//   ht_meta       each row's source token and remapped top-k ids and weights,
+//                 one thread per (token, rank, slot): coalesced stores from
+//                 T * R * k threads rather than per-lane scattered ones from
+//                 the few blocks of ht_rows
 //   copy          the bf16 copy kernel of ep_dispatch, driven by the [T, R]
 //                 map token_rank_row instead of the [T, k] token_row
 #include "../../include/ep.h"
@@ -53,10 +56,8 @@ __global__ __launch_bounds__(kHtTile) void ht_tile_hist_kernel(const int64_t* __
 }
 
 __global__ __launch_bounds__(kHtTile) void ht_rows_kernel(
-    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int64_t T,
-    int k, int E, int R, int ntiles, const int32_t* __restrict__ hist,
-    int32_t* __restrict__ token_rank_row, int32_t* __restrict__ recv_src_idx,
-    int64_t* __restrict__ recv_topk_idx, float* __restrict__ recv_w,
+    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, int ntiles,
+    const int32_t* __restrict__ hist, int32_t* __restrict__ token_rank_row,
     int32_t* __restrict__ rank_offset) {
     __shared__ int32_t base[EP_MAX_RANKS];                 // first row of rank r for this tile
     __shared__ int32_t wcnt[kHtWaves][EP_MAX_RANKS];       // per-wave counts -> offsets
@@ -66,8 +67,6 @@ __global__ __launch_bounds__(kHtTile) void ht_rows_kernel(
     const int epr = E / R;
     const int64_t t = static_cast<int64_t>(c) * kHtTile + threadIdx.x;
     const bool in = t < T;
-    // This token's mask (its ids are loaded here; they and the weights are
-    // read again, from L2, when the rows are written).
     const uint64_t m = in ? rank_mask(topk_idx + t * k, k, E, epr) : 0;
 
     // Per rank: tokens in all tiles and in the tiles before this one.
@@ -119,24 +118,39 @@ __global__ __launch_bounds__(kHtTile) void ht_rows_kernel(
     if (!in) return;
     // Lanes past the last token have m == 0, so they add nothing to a ballot
     // whether or not they take part in it.
-    const int64_t* ids = topk_idx + t * k;
     for (int r = 0; r < R; ++r) {
         const uint64_t b = ballot((m >> r) & 1);
         int row = -1;
         if ((m >> r) & 1) row = wcnt[wave][r] + __popcll(b & lanes_below());
         token_rank_row[t * R + r] = row;
-        if (row >= 0) {
-            recv_src_idx[row] = static_cast<int32_t>(t);
-            for (int j = 0; j < k; ++j) {
-                const int64_t e = ids[j];
-                const bool local = e >= 0 && e < E && e / epr == r;
-                recv_topk_idx[static_cast<int64_t>(row) * k + j] =
-                    local ? e - static_cast<int64_t>(r) * epr : -1;
-                if (recv_w)
-                    recv_w[static_cast<int64_t>(row) * k + j] =
-                        (local && topk_weights) ? topk_weights[t * k + j] : 0.0f;
-            }
-        }
+    }
+}
+
+
+// Per-row records: one thread per (token t, rank r, top-k slot j), k
+// consecutive threads per (t, r), so the k ids and weights of a row go out as
+// one contiguous store per wave.
+__global__ __launch_bounds__(256) void ht_meta_kernel(
+    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights,
+    const int32_t* __restrict__ token_rank_row, int32_t* __restrict__ recv_src_idx,
+    int64_t* __restrict__ recv_topk_idx, float* __restrict__ recv_w, int64_t T, int k, int E,
+    int R) {
+    const int epr = E / R;
+    const int64_t n = T * R * k;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const int64_t tr = i / k;            // t * R + r
+        const int j = static_cast<int>(i - tr * k);
+        const int row = token_rank_row[tr];
+        if (row < 0) continue;
+        const int64_t t = tr / R;
+        const int r = static_cast<int>(tr - t * R);
+        const int64_t e = topk_idx[t * k + j];
+        const bool local = e >= 0 && e < E && e / epr == r;
+        recv_topk_idx[static_cast<int64_t>(row) * k + j] = local ? e - static_cast<int64_t>(r) * epr : -1;
+        if (recv_w)
+            recv_w[static_cast<int64_t>(row) * k + j] = (local && topk_weights) ? topk_weights[t * k + j] : 0.0f;
+        if (j == 0) recv_src_idx[row] = static_cast<int32_t>(t);
     }
 }
 
@@ -164,9 +178,14 @@ hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const floa
     int32_t* hist = static_cast<int32_t*>(workspace);
     hipLaunchKernelGGL(ht_tile_hist_kernel, dim3(ntiles), dim3(kHtTile), 0, stream, topk_idx, T, k,
                        E, R, hist);
-    hipLaunchKernelGGL(ht_rows_kernel, dim3(ntiles), dim3(kHtTile), 0, stream, topk_idx,
-                       (recv_w ? topk_weights : nullptr), T, k, E, R, ntiles, hist, token_rank_row,
-                       recv_src_idx, recv_topk_idx, recv_w, rank_offset);
+    hipLaunchKernelGGL(ht_rows_kernel, dim3(ntiles), dim3(kHtTile), 0, stream, topk_idx, T, k, E,
+                       R, ntiles, hist, token_rank_row, rank_offset);
+    const int64_t n = T * R * k;
+    const int64_t blocks = ceil_div(n, 256);
+    const int64_t cap = kMaxLaunchThreads / 256;
+    hipLaunchKernelGGL(ht_meta_kernel, dim3(static_cast<unsigned>(blocks < cap ? blocks : cap)),
+                       dim3(256), 0, stream, topk_idx, topk_weights, token_rank_row, recv_src_idx,
+                       recv_topk_idx, recv_w, T, k, E, R);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_dispatch_copy_bf16(x, token_rank_row, recv_x, T * R, T, H, R, stream);

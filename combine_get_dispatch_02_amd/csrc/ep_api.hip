@@ -127,6 +127,8 @@ int ep_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weight
                                   num_ranks, recv_x, recv_src_idx, recv_expert_offset, token_row,
                                   workspace ? workspace_bytes : 0);
     if (s != EP_OK) return s;
+    if (!ep::copy_launch_fits(num_tokens, hidden, num_topk))
+        return fail(EP_ERR_UNSUPPORTED, "%s: num_tokens * hidden too large for one copy launch", fn);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (ep::dispatch_is_small(num_tokens, num_topk))
         return hip_status(ep::launch_dispatch_small_bf16(x, topk_idx, topk_weights, num_tokens, hidden,
@@ -198,6 +200,8 @@ int ep_dispatch_cached(const void* x, const int32_t* token_row, int64_t num_toke
         return fail(EP_ERR_INVALID_ARGUMENT, "%s: recv_x is NULL", fn);
     if (num_tokens > 0 && (!aligned16(x) || (recv_rows > 0 && !aligned16(recv_x))))
         return fail(EP_ERR_INVALID_ARGUMENT, "%s: x and recv_x must be 16-byte aligned", fn);
+    if (!ep::copy_launch_fits(num_tokens, hidden, num_topk))
+        return fail(EP_ERR_UNSUPPORTED, "%s: num_tokens * hidden too large for one copy launch", fn);
     if (num_tokens == 0 || recv_rows == 0) return EP_OK;
     return hip_status(ep::launch_dispatch_copy_bf16(x, token_row, recv_x, recv_rows, num_tokens,
                                                     hidden, num_topk, static_cast<hipStream_t>(stream)),
@@ -245,6 +249,8 @@ int ep_dispatch_ht(const void* x, const int64_t* topk_idx, const float* topk_wei
         return fail(EP_ERR_INVALID_ARGUMENT, "%s: hidden must be a positive multiple of 8", fn);
     if (num_tokens * static_cast<int64_t>(num_ranks) > INT32_MAX)
         return fail(EP_ERR_UNSUPPORTED, "%s: num_tokens * num_ranks >= 2^31", fn);
+    if (!ep::copy_launch_fits(num_tokens, hidden, num_ranks))
+        return fail(EP_ERR_UNSUPPORTED, "%s: num_tokens * hidden too large for one copy launch", fn);
     if (!recv_rank_offset) return fail(EP_ERR_INVALID_ARGUMENT, "%s: recv_rank_offset is NULL", fn);
     if (num_tokens > 0 && (!x || !recv_x || !recv_src_idx || !recv_topk_idx || !token_rank_row))
         return fail(EP_ERR_INVALID_ARGUMENT, "%s: a required pointer is NULL", fn);

@@ -44,6 +44,16 @@ hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weig
 
 // ---- small batches: receive order + copy in one launch -------------------------
 bool dispatch_is_small(int64_t T, int k);
+
+// A dispatch packet carries the grid's work-item count per dimension in 32
+// bits, so one launch holds at most this many threads in x.  Grid-stride
+// kernels cap their grid below it; the one-block-per-(token, segment) bf16
+// copies cannot, and their callers reject shapes beyond it.
+constexpr int64_t kMaxLaunchThreads = 0xFFFFFFFFll;
+// 16-byte vectors per lane per destination row in the bf16 copies (2 KB of a
+// row per wave); copy_launch_fits assumes it.
+constexpr int kCopyVec = 2;
+bool copy_launch_fits(int64_t T, int H, int fanout);
 hipError_t launch_dispatch_small_bf16(const void* x, const int64_t* topk_idx,
                                       const float* topk_weights, int64_t T, int H, int k, int E,
                                       int R, void* recv_x, int32_t* recv_src_idx, float* recv_w,

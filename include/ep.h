@@ -73,6 +73,11 @@ typedef enum {
 #define EP_MAX_TOPK 64          /* num_topk                                   */
 #define EP_MAX_RANKS 64         /* num_ranks                                  */
 #define EP_MAX_EXPERTS 2048     /* num_experts                                */
+/* The bf16 copies (ep_dispatch, ep_dispatch_cached, ep_dispatch_ht) run in one
+ * launch of T * ceil(H / 1024) blocks of 64 * min(fanout, 8) threads, where
+ * fanout is num_topk (num_ranks for ep_dispatch_ht); a launch holds at most
+ * 2^32 - 1 threads, and larger shapes return EP_ERR_UNSUPPORTED before any
+ * work is enqueued (e.g. T = 2^20 tokens of H = 8192 at fanout 8). */
 
 /* Static description of a status code; never NULL. */
 const char* ep_status_string(int status);
@@ -127,8 +132,9 @@ int ep_get_dispatch_layout(const int64_t* topk_idx, int64_t num_tokens, int num_
  *   recv_rank_offset   [R+1]   int32 out: recv_expert_offset[r*E/R] (may be NULL)
  *   token_row          [T, k]  int32 out: row of slot (t,j), -1 if empty
  *
- * Requires H % 8 == 0 (rows are whole 16-byte vectors), T*k < 2^31, and the
- * layout limits above.  Workspace: ep_dispatch_workspace_bytes(T, k, E).
+ * Requires H % 8 == 0 (rows are whole 16-byte vectors), T*k < 2^31, the
+ * layout limits above and (bf16) the copy-launch limit.
+ * Workspace: ep_dispatch_workspace_bytes(T, k, E).
  * The offsets are computed from topk_idx itself, so no earlier call's output
  * is trusted and every write stays inside the buffers described above.
  * ------------------------------------------------------------------------- */
@@ -176,7 +182,8 @@ int ep_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_we
  *   recv_x      [recv_rows, H]  bf16  out (16-byte aligned)
  *   recv_x_fp8  [recv_rows, H]  uint8 out (16-byte aligned), recv_scales
  *               [recv_rows, H/128] fp32 out (FP8 variant)
- * Requires H % 8 == 0 (bf16) or H % 128 == 0 (FP8), 1 <= k <= EP_MAX_TOPK.
+ * Requires H % 8 == 0 (bf16) or H % 128 == 0 (FP8), 1 <= k <= EP_MAX_TOPK
+ * and (bf16) the copy-launch limit.
  * No workspace.  T == 0 or recv_rows == 0 enqueues nothing.
  * ------------------------------------------------------------------------- */
 int ep_dispatch_cached(const void* x, const int32_t* token_row, int64_t num_tokens, int hidden,
@@ -207,7 +214,8 @@ int ep_dispatch_fp8_cached(const void* x, const int32_t* token_row, int64_t num_
  * The matching combine is ep_combine(expert_out, rows, token_rank_row, NULL,
  * T, H, R, out): out[t] = bf16(sum over ranks, in rank order, of the rank's
  * row for t), each row holding that rank's already weighted partial result.
- * Requires H % 8 == 0, T*R < 2^31 and the routing limits above.
+ * Requires H % 8 == 0, T*R < 2^31, the routing limits above and the
+ * copy-launch limit with fanout R.
  * Workspace: ep_dispatch_ht_workspace_bytes(T, R).
  * ------------------------------------------------------------------------- */
 size_t ep_dispatch_ht_workspace_bytes(int64_t num_tokens, int num_ranks);

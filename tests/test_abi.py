@@ -169,3 +169,16 @@ def test_dispatch_ht_rejects(kw, code):
 def test_ht_workspace_size():
     assert ep.ep_dispatch_ht_workspace_bytes(4096, 8) >= 16 * 8 * 4
     assert ep.ep_dispatch_ht_workspace_bytes(-1, 8) == 0
+
+
+def test_copy_launch_limit_rejected_before_any_launch():
+    """The bf16 copies launch one block of min(fanout, 8) waves per (token,
+    2 KB column segment); a launch holds at most 2^32 - 1 threads.  At
+    T = 2^20, H = 8192 (8 segments), fanout 8 that is exactly 2^32: rejected
+    as unsupported, before anything is enqueued (fake pointers here)."""
+    big = dict(T=2 ** 20, H=8192, k=8, E=8, R=8, wsb=1 << 40)
+    assert _dispatch(**big) == EUNSUP
+    assert b"too large for one copy launch" in ep.lib().ep_last_error()
+    assert _ht(**big) == EUNSUP
+    st = ep.lib().ep_dispatch_cached(FAKE, FAKE, 2 ** 20, 8192, 8, FAKE, 2 ** 23, None)
+    assert st == EUNSUP
