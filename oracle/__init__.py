@@ -53,6 +53,8 @@ def _load() -> ctypes.CDLL:
     lib.oracle_dispatch_cached.argtypes = [P, P, i64, i32, i32, P, i64]
     lib.oracle_dispatch_ht.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P]
     lib.oracle_dispatch_fp8_cached.argtypes = [P, P, i64, i32, i32, P, P, i64]
+    lib.oracle_dispatch_ll.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P]
+    lib.oracle_dispatch_ll_fp8.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P]
     lib.oracle_quantize_row.argtypes = [P, i32, P, P]
     lib.oracle_e4m3_encode_array.argtypes = [P, i64, P]
     lib.oracle_bf16_rne_array.argtypes = [P, i64, P]
@@ -60,7 +62,7 @@ def _load() -> ctypes.CDLL:
     lib.oracle_e4m3_decode.restype = ctypes.c_float
     for f in ("oracle_layout", "oracle_dispatch", "oracle_dispatch_fp8", "oracle_combine",
               "oracle_quantize_row", "oracle_dispatch_cached", "oracle_dispatch_fp8_cached",
-              "oracle_dispatch_ht"):
+              "oracle_dispatch_ht", "oracle_dispatch_ll", "oracle_dispatch_ll_fp8"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -78,7 +80,7 @@ def _use_library(path: Optional[str]) -> None:
         for f in ("oracle_layout", "oracle_dispatch", "oracle_dispatch_fp8", "oracle_combine",
                   "oracle_quantize_row", "oracle_e4m3_encode_array", "oracle_bf16_rne_array",
                   "oracle_e4m3_decode", "oracle_dispatch_cached", "oracle_dispatch_fp8_cached",
-                  "oracle_dispatch_ht"):
+                  "oracle_dispatch_ht", "oracle_dispatch_ll", "oracle_dispatch_ll_fp8"):
             getattr(lib, f).argtypes = getattr(_lib, f).argtypes
             getattr(lib, f).restype = getattr(_lib, f).restype
         _lib = lib
@@ -160,6 +162,51 @@ def dispatch_ht(x: np.ndarray, topk_idx: np.ndarray, topk_weights: Optional[np.n
     _check(rc, "oracle_dispatch_ht")
     return dict(recv_x=recv_x, recv_src_idx=src, recv_topk_idx=ridx, recv_topk_weights=rw,
                 recv_rank_offset=roff, token_rank_row=trr)
+
+
+def dispatch_ll(x: np.ndarray, topk_idx: np.ndarray, topk_weights: Optional[np.ndarray],
+                num_experts: int, capacity: int, sentinel: int = 0):
+    """Padded expert-major dispatch: recv_x [E, capacity, H]; rows an expert
+    does not fill keep `sentinel` (src -2, weights NaN)."""
+    x = _c(x, np.uint16)
+    idx = _c(topk_idx, np.int64)
+    T, k = idx.shape
+    H = x.shape[1]
+    E = num_experts
+    recv_x = np.full((E, capacity, H), sentinel, np.uint16)
+    cnt = np.full(E, -7, np.int32)
+    src = np.full((E, capacity), -2, np.int32)
+    rw = np.full((E, capacity), np.nan, np.float32) if topk_weights is not None else None
+    slot = np.zeros((T, k), np.int32)
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    rc = _load().oracle_dispatch_ll(_p(x), _p(idx), _p(w), T, H, k, E, capacity, _p(recv_x),
+                                    _p(cnt), _p(src), _p(rw), _p(slot))
+    _check(rc, "oracle_dispatch_ll")
+    return dict(recv_x=recv_x, recv_count=cnt, recv_src_idx=src, recv_topk_weights=rw,
+                token_slot=slot)
+
+
+def dispatch_ll_fp8(x: np.ndarray, topk_idx: np.ndarray, topk_weights: Optional[np.ndarray],
+                    num_experts: int, capacity: int):
+    """Padded expert-major FP8 dispatch: codes [E, capacity, H], scales
+    [E, capacity, H/128]; unfilled rows keep codes 0 and scales NaN."""
+    x = _c(x, np.uint16)
+    idx = _c(topk_idx, np.int64)
+    T, k = idx.shape
+    H = x.shape[1]
+    E = num_experts
+    q = np.zeros((E, capacity, H), np.uint8)
+    sc = np.full((E, capacity, H // 128), np.nan, np.float32)
+    cnt = np.full(E, -7, np.int32)
+    src = np.full((E, capacity), -2, np.int32)
+    rw = np.full((E, capacity), np.nan, np.float32) if topk_weights is not None else None
+    slot = np.zeros((T, k), np.int32)
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    rc = _load().oracle_dispatch_ll_fp8(_p(x), _p(idx), _p(w), T, H, k, E, capacity, _p(q), _p(sc),
+                                        _p(cnt), _p(src), _p(rw), _p(slot))
+    _check(rc, "oracle_dispatch_ll_fp8")
+    return dict(recv_x_fp8=q, recv_scales=sc, recv_count=cnt, recv_src_idx=src,
+                recv_topk_weights=rw, token_slot=slot)
 
 
 def dispatch_fp8(x: np.ndarray, topk_idx: np.ndarray, topk_weights: Optional[np.ndarray],

@@ -351,6 +351,98 @@ int oracle_dispatch_fp8_cached(const uint16_t* x, const int32_t* token_row, int6
     return ORC_OK;
 }
 
+/* Low-latency padded receive layout: page "[Not ready] MSCCLPP EP
+ * implementation #852" -- the LL benchmark's receive buffer (the commit that
+ * stops cloning the ~58 MB dispatch receive buffer: one expert region per
+ * local expert, each sized for a fixed number of tokens per source) and the
+ * low-latency runtime's rank-major / expert-major tests at capacities 1 and 2.
+ * With one source the receive buffer is [E, capacity, H]: expert e owns rows
+ * e*capacity .. e*capacity + capacity - 1, filled from the front in (t, j)
+ * order; a slot that finds its expert's region full is dropped.
+ *   recv_count[e]               = min(#valid slots with expert e, capacity)
+ *   token_slot[t, j]            = e*capacity + (its position among expert e's
+ *                                 slots in (t, j) order) if that position is
+ *                                 below capacity, else -1 (also -1 if empty)
+ *   recv_x[slot, :]             = x[t, :]
+ *   recv_src_idx[slot]          = t
+ *   recv_topk_weights[slot]     = topk_weights[t, j]
+ * Rows from recv_count[e] to capacity - 1 of each expert are not written. */
+static int check_ll_args(const void* x, const int64_t* topk_idx, int64_t T, int H, int k, int E,
+                         int capacity, const void* recv, const int32_t* recv_count,
+                         const int32_t* recv_src_idx, const int32_t* token_slot)
+{
+    if (T < 0 || H < 1 || k < 1 || E < 1 || capacity < 1) return 0;
+    if ((int64_t)E * capacity > INT32_MAX) return 0;
+    if (!recv_count) return 0;
+    if (T > 0 && (!x || !topk_idx || !recv || !recv_src_idx || !token_slot)) return 0;
+    return 1;
+}
+
+static void assign_ll_slots(const int64_t* topk_idx, int64_t T, int k, int E, int capacity,
+                            int32_t* recv_count, int32_t* token_slot, int32_t* recv_src_idx,
+                            const float* topk_weights, float* recv_topk_weights)
+{
+    for (int e = 0; e < E; ++e) recv_count[e] = 0;
+    int64_t* seen = (int64_t*)calloc((size_t)E, sizeof(int64_t));   /* slots met so far */
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int64_t e = topk_idx[t * k + j];
+            token_slot[t * k + j] = -1;
+            if (!slot_valid(e, E)) continue;
+            int64_t pos = seen[e]++;
+            if (pos >= capacity) continue;
+            int32_t slot = (int32_t)(e * capacity + pos);
+            token_slot[t * k + j] = slot;
+            recv_count[e] = (int32_t)(pos + 1);
+            recv_src_idx[slot] = (int32_t)t;
+            if (topk_weights && recv_topk_weights) recv_topk_weights[slot] = topk_weights[t * k + j];
+        }
+    free(seen);
+}
+
+int oracle_dispatch_ll(const uint16_t* x, const int64_t* topk_idx, const float* topk_weights,
+                       int64_t T, int H, int k, int E, int capacity, uint16_t* recv_x,
+                       int32_t* recv_count, int32_t* recv_src_idx, float* recv_topk_weights,
+                       int32_t* token_slot)
+{
+    if (!check_ll_args(x, topk_idx, T, H, k, E, capacity, recv_x, recv_count, recv_src_idx,
+                       token_slot))
+        return ORC_EINVAL;
+    assign_ll_slots(topk_idx, T, k, E, capacity, recv_count, token_slot, recv_src_idx,
+                    topk_weights, recv_topk_weights);
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int32_t slot = token_slot[t * k + j];
+            if (slot < 0) continue;
+            memcpy(recv_x + (int64_t)slot * H, x + t * (int64_t)H, sizeof(uint16_t) * (size_t)H);
+        }
+    return ORC_OK;
+}
+
+/* The same padded layout holding the per-token FP8 cast of
+ * oracle_quantize_row: codes [E, capacity, H], scales [E, capacity, H/128]. */
+int oracle_dispatch_ll_fp8(const uint16_t* x, const int64_t* topk_idx, const float* topk_weights,
+                           int64_t T, int H, int k, int E, int capacity, uint8_t* recv_x_fp8,
+                           float* recv_scales, int32_t* recv_count, int32_t* recv_src_idx,
+                           float* recv_topk_weights, int32_t* token_slot)
+{
+    if (!check_ll_args(x, topk_idx, T, H, k, E, capacity, recv_x_fp8, recv_count, recv_src_idx,
+                       token_slot))
+        return ORC_EINVAL;
+    if (H % 128 != 0 || (T > 0 && !recv_scales)) return ORC_EINVAL;
+    assign_ll_slots(topk_idx, T, k, E, capacity, recv_count, token_slot, recv_src_idx,
+                    topk_weights, recv_topk_weights);
+    const int nb = H / 128;
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int32_t slot = token_slot[t * k + j];
+            if (slot < 0) continue;
+            oracle_quantize_row(x + t * (int64_t)H, H, recv_x_fp8 + (int64_t)slot * H,
+                                recv_scales + (int64_t)slot * nb);
+        }
+    return ORC_OK;
+}
+
 /* High-throughput (rank-deduplicated) dispatch: page "[Not ready] MSCCLPP EP
  * implementation #852", PR body "Scope / Intranode" (intranode dispatch sends
  * each token once to every rank that hosts at least one of its experts; the

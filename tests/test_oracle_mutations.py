@@ -15,6 +15,7 @@ import oracle
 import test_oracle_combine as tc
 import test_oracle_fp8 as tf
 import test_oracle_ht as th
+import test_oracle_ll as tll
 import test_oracle_layout_rows as tl
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ep_oracle.c")
@@ -48,6 +49,19 @@ def _ht_pins():
     for name in ("tiny", "large"):
         th.test_weights_and_slots_conserved(name)
     th.test_unweighted_combine_closed_form()
+
+
+def _ll_pins():
+    tll.test_hand_worked_example()
+    for i in range(len(tl.ROUTINGS)):
+        for cap in tll.CAPS:
+            tll.test_matches_brute_force(i, cap)
+    for name in ("tiny", "ll_fp8"):
+        tll.test_no_drop_is_the_packed_dispatch_per_expert(name)
+    for cap in (1, 2, 5):
+        tll.test_drops_are_the_latest_slots_and_conserved(cap)
+    tll.test_fp8_rows_hold_the_token_cast()
+    tll.test_combine_over_padded_map_equals_packed_combine()
 
 
 def _fp8_pins():
@@ -148,6 +162,17 @@ MUTATIONS = {
                              _ht_pins),
     "combine_unweighted_zero": ("const float wj = topk_weights ? topk_weights[t * k + j] : 1.0f;",
                                 "const float wj = topk_weights ? topk_weights[t * k + j] : 0.5f;", _ht_pins),
+    # padded expert-major (low-latency) dispatch
+    "ll_capacity_off_by_one": ("if (pos >= capacity) continue;", "if (pos > capacity) continue;", _ll_pins),
+    "ll_position_major": ("int32_t slot = (int32_t)(e * capacity + pos);",
+                          "int32_t slot = (int32_t)(pos * E + e);", _ll_pins),
+    "ll_count_unclamped": ("if (pos >= capacity) continue;",
+                           "recv_count[e] = (int32_t)(pos + 1);\n            if (pos >= capacity) continue;",
+                           _ll_pins),
+    "ll_weight_first_slot": ("recv_topk_weights[slot] = topk_weights[t * k + j];",
+                             "recv_topk_weights[slot] = topk_weights[t * k];", _ll_pins),
+    "ll_fp8_scale_row": ("recv_scales + (int64_t)slot * nb);",
+                         "recv_scales + (int64_t)(slot / 2) * nb);", _ll_pins),
     "bf16_widen_shift": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;", _combine_pins),
 }
 
@@ -171,5 +196,5 @@ def test_planted_mistake_is_caught(name, tmp_path):
 
 
 def test_unmutated_oracle_passes_all_pins():
-    for pins in (_layout_pins, _row_pins, _fp8_pins, _combine_pins, _cached_pins, _ht_pins):
+    for pins in (_layout_pins, _row_pins, _fp8_pins, _combine_pins, _cached_pins, _ht_pins, _ll_pins):
         pins()
