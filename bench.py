@@ -6,7 +6,11 @@ input already resident in HBM:
     ep_get_dispatch_layout -> ep_dispatch -> ep_combine -> ep_dispatch_fp8
 with the combine fed the dispatched rows (identity experts), followed by the
 rank-deduplicated pair ep_dispatch_ht -> ep_combine (unweighted, over the
-per-rank rows), reported as extra phases beside the headline.  Before each
+per-rank rows) and the padded expert-major (low-latency) layout
+ep_dispatch_ll -> ep_combine (over the slot map) -> ep_dispatch_ll_fp8, with
+the capacity set to the busiest expert's load rounded up to 64 rows (nothing
+dropped), all reported
+as extra phases beside the headline.  Before each
 phase (outside its events) a 512 MiB write followed by a 512 MiB read of
 another buffer evicts L2 and the 256 MB Infinity Cache: the phase's inputs
 are then only in HBM and the caches hold clean, unrelated lines, so no
@@ -61,11 +65,21 @@ def ht_rows(wl, idx):
     return int(hit.sum())
 
 
-def algorithmic_bytes(wl, n_ht=None):
+def ll_capacity(wl, idx):
+    """Capacity that drops nothing: the busiest expert's load rounded up to a
+    multiple of 64 rows, the M-tile of a grouped GEMM over [capacity, H]."""
+    import numpy as np
+    valid = idx[(idx >= 0) & (idx < wl.E)]
+    busiest = int(np.bincount(valid, minlength=wl.E).max()) if valid.size else 1
+    return (max(busiest, 1) + 63) // 64 * 64
+
+
+def algorithmic_bytes(wl, n_ht=None, n_ll=None):
     """Bytes each call must move at least (read once, write once)."""
     T, H, k, E, R, G = wl.T, wl.H, wl.k, wl.E, wl.R, wl.G
     N = T * k
     n = T * R if n_ht is None else n_ht
+    m = N if n_ll is None else n_ll                                  # slots kept by the padded layout
     ht_maps = 4 * T * R + 4 * n + 8 * n * k + 4 * n * k + 4 * (R + 1)   # token_rank_row, src, ids, w
     maps = 4 * N + 4 * N + 4 * T * k + 4 * (E + 1) + 4 * (R + 1)   # src, recv_w, token_row, offsets
     reads = 8 * T * k + 4 * T * k                                  # topk_idx, topk_weights
@@ -76,6 +90,11 @@ def algorithmic_bytes(wl, n_ht=None):
         combine=4 * T * k + 4 * T * k + 2 * N * H + 2 * T * H,
         dispatch_ht=8 * T * k + 4 * T * k + 2 * T * H + 2 * n * H + ht_maps,
         combine_ht=4 * T * R + 2 * n * H + 2 * T * H,
+        # padded layout, m slots kept: token_slot, src and weight per kept
+        # slot, the E counts
+        dispatch_ll=reads + 2 * T * H + 2 * m * H + 4 * T * k + 8 * m + 4 * E,
+        combine_ll=4 * T * k + 4 * T * k + 2 * m * H + 2 * T * H,
+        dispatch_ll_fp8=reads + 2 * T * H + m * H + 4 * m * (H // 128) + 4 * T * k + 8 * m + 4 * E,
     )
 
 
@@ -208,6 +227,9 @@ def main():
                     help="instead of the headline: time one whole step (layout, dispatch, combine, "
                          "FP8 dispatch; no cache eviction) replayed from a captured HIP graph "
                          "against the same step launched eagerly")
+    ap.add_argument("--ll-capacity", type=int, default=0,
+                    help="capacity (rows per expert) of the padded-layout phases; default: the "
+                         "busiest expert's load rounded up to 64 rows")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after the timed steps, run 4 plain 256 MiB device copies (a known-size "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -267,10 +289,26 @@ def main():
     ws_ht = torch.empty(ep.ep_dispatch_ht_workspace_bytes(T, R), dtype=torch.uint8, device=dev)
     comb_ht = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     n_ht = ht_rows(wl, idx)
+    cap_ll = args.ll_capacity or ll_capacity(wl, idx)
+    n_ll = int(np.minimum(np.bincount(idx[(idx >= 0) & (idx < E)], minlength=E), cap_ll).sum())
+    ll = dict(recv_x=torch.empty((E, cap_ll, H), dtype=torch.bfloat16, device=dev),
+              recv_count=torch.empty(E, dtype=torch.int32, device=dev),
+              recv_src_idx=torch.empty((E, cap_ll), dtype=torch.int32, device=dev),
+              recv_topk_weights=torch.empty((E, cap_ll), dtype=torch.float32, device=dev),
+              token_slot=torch.empty((T, k), dtype=torch.int32, device=dev))
+    ll8 = dict(recv_x_fp8=torch.empty((E, cap_ll, H), dtype=torch.uint8, device=dev),
+               recv_scales=torch.empty((E, cap_ll, H // 128), dtype=torch.float32, device=dev),
+               recv_count=torch.empty(E, dtype=torch.int32, device=dev),
+               recv_src_idx=torch.empty((E, cap_ll), dtype=torch.int32, device=dev),
+               recv_topk_weights=torch.empty((E, cap_ll), dtype=torch.float32, device=dev),
+               token_slot=torch.empty((T, k), dtype=torch.int32, device=dev))
+    ws_ll = torch.empty(ep.ep_dispatch_ll_workspace_bytes(T, k, E), dtype=torch.uint8, device=dev)
+    comb_ll = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     flush_src = torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
 
-    phases = ["layout", "dispatch", "combine", "dispatch_fp8", "dispatch_ht", "combine_ht"]
+    phases = ["layout", "dispatch", "combine", "dispatch_fp8", "dispatch_ht", "combine_ht",
+              "dispatch_ll", "combine_ll", "dispatch_ll_fp8"]
 
     def flush(i):
         if not args.no_flush:
@@ -300,9 +338,21 @@ def main():
         ev[9].record()
         ep.ep_combine(ht["recv_x"], ht["token_rank_row"], None, num_rows=n_ht, out=comb_ht)
         ev[10].record()
+        flush(i + 5)
+        ev[11].record()
+        ep.ep_dispatch_ll(xd, idxd, wd, E, cap_ll, out=ll, workspace=ws_ll)
+        ev[12].record()
+        flush(i + 6)
+        ev[13].record()
+        ep.ep_combine(ll["recv_x"].view(E * cap_ll, H), ll["token_slot"], wd, out=comb_ll)
+        ev[14].record()
+        flush(i + 7)
+        ev[15].record()
+        ep.ep_dispatch_ll_fp8(xd, idxd, wd, E, cap_ll, out=ll8, workspace=ws_ll)
+        ev[16].record()
 
     def events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(11)]
+        return [torch.cuda.Event(enable_timing=True) for _ in range(17)]
 
     if args.graph:
         graph_mode(args, wl, ep, torch, np, idxd, xd, wd, lay, ws_l, disp, ws_d, comb, fp8)
@@ -315,6 +365,8 @@ def main():
         raise RuntimeError("dispatch filled an unexpected number of rows")
     if ht["recv_rank_offset"][-1].item() != n_ht:
         raise RuntimeError("rank-deduplicated dispatch filled an unexpected number of rows")
+    if ll["recv_count"].sum().item() != n_ll or ll8["recv_count"].sum().item() != n_ll:
+        raise RuntimeError("padded dispatch filled an unexpected number of slots")
 
     evs = [events() for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -333,13 +385,16 @@ def main():
         torch.cuda.synchronize()
 
     ms = {p: np.array([e[a].elapsed_time(e[b]) for e in evs])
-          for p, (a, b) in zip(phases, [(0, 1), (1, 2), (3, 4), (5, 6), (7, 8), (9, 10)])}
-    B = algorithmic_bytes(wl, n_ht)
+          for p, (a, b) in zip(phases, [(0, 1), (1, 2), (3, 4), (5, 6), (7, 8), (9, 10), (11, 12),
+                                        (13, 14), (15, 16)])}
+    B = algorithmic_bytes(wl, n_ht, n_ll)
     t_dc = float(ms["dispatch"].sum() + ms["combine"].sum()) / 1e3
     value = (B["dispatch"] + B["combine"]) * args.steps / t_dc / 1e9
     step_ms = float(sum(ms[p].mean() for p in phases[:4]))
     t_ht = float(ms["dispatch_ht"].sum() + ms["combine_ht"].sum()) / 1e3
     ht_gbs = (B["dispatch_ht"] + B["combine_ht"]) * args.steps / t_ht / 1e9
+    t_ll = float(ms["dispatch_ll"].sum() + ms["combine_ll"].sum()) / 1e3
+    ll_gbs = (B["dispatch_ll"] + B["combine_ll"]) * args.steps / t_ll / 1e9
     phase_info = {}
     for p in phases:
         us = ms[p] * 1e3
@@ -386,6 +441,14 @@ def main():
                        "pct_of_hbm_peak": round(100 * ht_gbs / HBM_PEAK_GBS, 2),
                        "us_per_pair": round(1e6 * t_ht / args.steps, 2),
                        "note": "ep_dispatch_ht + unweighted ep_combine; not part of value or ms_per_step"},
+        "ll_padded": {"capacity": cap_ll, "slots_filled": n_ll, "slots_dropped": N - n_ll,
+                      "slots_allocated": E * cap_ll,
+                      "dispatch_plus_combine_GBps": round(ll_gbs, 1),
+                      "pct_of_hbm_peak": round(100 * ll_gbs / HBM_PEAK_GBS, 2),
+                      "us_per_pair": round(1e6 * t_ll / args.steps, 2),
+                      "note": "ep_dispatch_ll + ep_combine over token_slot, capacity = busiest "
+                              "expert's load rounded up to 64 rows (nothing dropped); not part of "
+                              "value or ms_per_step"},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libep.so")
-SOURCES = ["ep_api.hip", "layout.hip", "dispatch.hip", "dispatch_ht.hip", "combine.hip"]
+SOURCES = ["ep_api.hip", "layout.hip", "dispatch.hip", "dispatch_ht.hip", "dispatch_ll.hip",
+           "combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -458,6 +458,9 @@ __global__ __launch_bounds__(256) void copy_fp8_kernel(const u32x4* __restrict__
 // round trip that overlaps the block's x loads, and no index launch precedes
 // the copy.  The token's first block writes its token_row / recv_src_idx /
 // recv_topk_weights; block 0 writes the offsets.
+// With cap > 0 the same blocks fill the padded expert-major layout instead:
+// the slot of (t, j) is e*cap + (its position among expert e's slots), or -1
+// from position cap on, and block 0 writes recv_count[e] = min(count, cap).
 // LDS: cnt_pre[E], cnt_all[E], wave_tot[16], own[EP_MAX_TOPK], rows[EP_MAX_TOPK].
 constexpr int kSmallMaxK = 64;
 
@@ -498,11 +501,12 @@ __device__ int block_exclusive_scan_rt(int32_t* a, int n, int32_t* wave_tot) {
 // every thread of the block.
 __device__ void small_token_rows(const int64_t* __restrict__ topk_idx,
                                  const float* __restrict__ topk_weights, int64_t T, int k, int E,
-                                 int R, int64_t t, bool write_maps, bool write_offs,
+                                 int R, int cap, int64_t t, bool write_maps, bool write_offs,
                                  int32_t* __restrict__ token_row,
                                  int32_t* __restrict__ recv_src_idx, float* __restrict__ recv_w,
                                  int32_t* __restrict__ expert_offset,
-                                 int32_t* __restrict__ rank_offset, int32_t* lds,
+                                 int32_t* __restrict__ rank_offset,
+                                 int32_t* __restrict__ recv_count, int32_t* lds,
                                  int32_t* rows_out) {
     int32_t* cnt_pre = lds;
     int32_t* cnt_all = lds + E;
@@ -529,15 +533,22 @@ __device__ void small_token_rows(const int64_t* __restrict__ topk_idx,
         if (sl >= first && sl < first + k) own[sl - first] = valid ? static_cast<int32_t>(e) : -1;
     }
     __syncthreads();
-    const int total = block_exclusive_scan_rt(cnt_all, E, wave_tot);
-    if (write_offs) write_offsets(cnt_all, total, E, R, expert_offset, rank_offset);
+    if (cap > 0) {
+        if (write_offs)
+            for (int e = threadIdx.x; e < E; e += blockDim.x) recv_count[e] = min(cnt_all[e], cap);
+    } else {
+        const int total = block_exclusive_scan_rt(cnt_all, E, wave_tot);
+        if (write_offs) write_offsets(cnt_all, total, E, R, expert_offset, rank_offset);
+    }
     if (j < k) {
         const int e = own[j];
         int row = -1;
         if (e >= 0) {
             int before = 0;
             for (int q = 0; q < j; ++q) before += own[q] == e;
-            row = cnt_all[e] + cnt_pre[e] + before;
+            const int pos = cnt_pre[e] + before;
+            if (cap <= 0) row = cnt_all[e] + pos;
+            else if (pos < cap) row = e * cap + pos;
         }
         rows_out[j] = row;
         if (write_maps) {
@@ -554,10 +565,11 @@ __device__ void small_token_rows(const int64_t* __restrict__ topk_idx,
 // bf16, small batches: the copy_bf16 block shape, rows derived in-block.
 __global__ __launch_bounds__(512) void dispatch_small_bf16_kernel(
     const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
-    const float* __restrict__ topk_weights, int64_t T, int k, int E, int R, int V, int kb,
-    int segs, u32x4* __restrict__ recv, int32_t* __restrict__ token_row,
+    const float* __restrict__ topk_weights, int64_t T, int k, int E, int R, int cap, int V,
+    int kb, int segs, u32x4* __restrict__ recv, int32_t* __restrict__ token_row,
     int32_t* __restrict__ recv_src_idx, float* __restrict__ recv_w,
-    int32_t* __restrict__ expert_offset, int32_t* __restrict__ rank_offset) {
+    int32_t* __restrict__ expert_offset, int32_t* __restrict__ rank_offset,
+    int32_t* __restrict__ recv_count) {
     extern __shared__ int32_t lds[];
     int32_t* rows = lds + 2 * E + 16 + kSmallMaxK;
     const int lane = lane_id();
@@ -571,8 +583,9 @@ __global__ __launch_bounds__(512) void dispatch_small_bf16_kernel(
         const int v = v0 + u * kWave;
         if (v < V) val[u] = x[t * V + v];
     }
-    small_token_rows(topk_idx, topk_weights, T, k, E, R, t, seg == 0, blockIdx.x == 0, token_row,
-                     recv_src_idx, recv_w, expert_offset, rank_offset, lds, rows);
+    small_token_rows(topk_idx, topk_weights, T, k, E, R, cap, t, seg == 0, blockIdx.x == 0,
+                     token_row, recv_src_idx, recv_w, expert_offset, rank_offset, recv_count, lds,
+                     rows);
     for (int j = w; j < k; j += kb) {
         const int r = rows[j];
         if (r < 0) continue;
@@ -589,11 +602,11 @@ __global__ __launch_bounds__(512) void dispatch_small_bf16_kernel(
 // wave quantises 1024 channels and stores them to every row of the token.
 __global__ __launch_bounds__(256) void dispatch_small_fp8_kernel(
     const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
-    const float* __restrict__ topk_weights, int64_t T, int k, int E, int R, int H, int segs,
-    uint8_t* __restrict__ recv_q, float* __restrict__ recv_scales,
+    const float* __restrict__ topk_weights, int64_t T, int k, int E, int R, int cap, int H,
+    int segs, uint8_t* __restrict__ recv_q, float* __restrict__ recv_scales,
     int32_t* __restrict__ token_row, int32_t* __restrict__ recv_src_idx,
     float* __restrict__ recv_w, int32_t* __restrict__ expert_offset,
-    int32_t* __restrict__ rank_offset) {
+    int32_t* __restrict__ rank_offset, int32_t* __restrict__ recv_count) {
     extern __shared__ int32_t lds[];
     int32_t* rows = lds + 2 * E + 16 + kSmallMaxK;
     const int lane = lane_id();
@@ -610,8 +623,9 @@ __global__ __launch_bounds__(256) void dispatch_small_fp8_kernel(
         a0 = __builtin_nontemporal_load(src);
         a1 = __builtin_nontemporal_load(src + 1);
     }
-    small_token_rows(topk_idx, topk_weights, T, k, E, R, t, seg == 0, blockIdx.x == 0, token_row,
-                     recv_src_idx, recv_w, expert_offset, rank_offset, lds, rows);
+    small_token_rows(topk_idx, topk_weights, T, k, E, R, cap, t, seg == 0, blockIdx.x == 0,
+                     token_row, recv_src_idx, recv_w, expert_offset, rank_offset, recv_count, lds,
+                     rows);
     float s;
     const u32x4 q = quantize16(a0, a1, s);
     if (!active) return;
@@ -690,32 +704,34 @@ bool copy_launch_fits(int64_t T, int H, int fanout) {
 
 hipError_t launch_dispatch_small_bf16(const void* x, const int64_t* topk_idx,
                                       const float* topk_weights, int64_t T, int H, int k, int E,
-                                      int R, void* recv_x, int32_t* recv_src_idx, float* recv_w,
-                                      int32_t* expert_offset, int32_t* rank_offset,
-                                      int32_t* token_row, hipStream_t stream) {
+                                      int R, int cap, void* recv_x, int32_t* recv_src_idx,
+                                      float* recv_w, int32_t* expert_offset, int32_t* rank_offset,
+                                      int32_t* recv_count, int32_t* token_row,
+                                      hipStream_t stream) {
     const int V = H / 8;
     const int segs = static_cast<int>(ceil_div(V, kCopyVec * kWave));
     const int kb = k < 8 ? k : 8;
     hipLaunchKernelGGL(dispatch_small_bf16_kernel, dim3(static_cast<unsigned>(T * segs)),
                        dim3(kb * kWave), small_lds_bytes(E), stream, static_cast<const u32x4*>(x),
-                       topk_idx, (recv_w ? topk_weights : nullptr), T, k, E, R, V, kb, segs,
+                       topk_idx, (recv_w ? topk_weights : nullptr), T, k, E, R, cap, V, kb, segs,
                        static_cast<u32x4*>(recv_x), token_row, recv_src_idx,
-                       (topk_weights ? recv_w : nullptr), expert_offset, rank_offset);
+                       (topk_weights ? recv_w : nullptr), expert_offset, rank_offset, recv_count);
     return hipGetLastError();
 }
 
 hipError_t launch_dispatch_small_fp8(const void* x, const int64_t* topk_idx,
                                      const float* topk_weights, int64_t T, int H, int k, int E,
-                                     int R, uint8_t* recv_q, float* recv_scales,
+                                     int R, int cap, uint8_t* recv_q, float* recv_scales,
                                      int32_t* recv_src_idx, float* recv_w,
                                      int32_t* expert_offset, int32_t* rank_offset,
-                                     int32_t* token_row, hipStream_t stream) {
+                                     int32_t* recv_count, int32_t* token_row,
+                                     hipStream_t stream) {
     const int segs = static_cast<int>(ceil_div(H, 4096));
     hipLaunchKernelGGL(dispatch_small_fp8_kernel, dim3(static_cast<unsigned>(T * segs)), dim3(256),
                        small_lds_bytes(E), stream, static_cast<const u32x4*>(x), topk_idx,
-                       (recv_w ? topk_weights : nullptr), T, k, E, R, H, segs, recv_q, recv_scales,
-                       token_row, recv_src_idx, (topk_weights ? recv_w : nullptr), expert_offset,
-                       rank_offset);
+                       (recv_w ? topk_weights : nullptr), T, k, E, R, cap, H, segs, recv_q,
+                       recv_scales, token_row, recv_src_idx, (topk_weights ? recv_w : nullptr),
+                       expert_offset, rank_offset, recv_count);
     return hipGetLastError();
 }
 

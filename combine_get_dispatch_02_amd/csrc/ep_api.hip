@@ -132,10 +132,10 @@ int ep_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weight
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (ep::dispatch_is_small(num_tokens, num_topk))
         return hip_status(ep::launch_dispatch_small_bf16(x, topk_idx, topk_weights, num_tokens, hidden,
-                                                         num_topk, num_experts, num_ranks, recv_x,
+                                                         num_topk, num_experts, num_ranks, 0, recv_x,
                                                          recv_src_idx, recv_topk_weights,
                                                          recv_expert_offset, recv_rank_offset,
-                                                         token_row, st),
+                                                         nullptr, token_row, st),
                           fn);
     s = hip_status(ep::launch_dispatch_index(topk_idx, topk_weights, num_tokens, num_topk,
                                              num_experts, num_ranks, recv_src_idx,
@@ -168,10 +168,10 @@ int ep_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_we
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (ep::dispatch_is_small(num_tokens, num_topk))
         return hip_status(ep::launch_dispatch_small_fp8(x, topk_idx, topk_weights, num_tokens, hidden,
-                                                        num_topk, num_experts, num_ranks, recv_x_fp8,
+                                                        num_topk, num_experts, num_ranks, 0, recv_x_fp8,
                                                         recv_scales, recv_src_idx, recv_topk_weights,
                                                         recv_expert_offset, recv_rank_offset,
-                                                        token_row, st),
+                                                        nullptr, token_row, st),
                           fn);
     s = hip_status(ep::launch_dispatch_index(topk_idx, topk_weights, num_tokens, num_topk,
                                              num_experts, num_ranks, recv_src_idx,
@@ -264,6 +264,65 @@ int ep_dispatch_ht(const void* x, const int64_t* topk_idx, const float* topk_wei
                                              recv_topk_idx, recv_topk_weights, recv_rank_offset,
                                              token_rank_row, workspace, static_cast<hipStream_t>(stream)),
                       fn);
+}
+
+size_t ep_dispatch_ll_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts) {
+    if (num_tokens < 0 || num_topk < 1 || num_experts < 1) return 0;
+    return ep::ll_workspace_bytes(num_tokens, num_topk, num_experts);
+}
+
+static int dispatch_ll_common(const char* fn, bool fp8, const void* x, const int64_t* topk_idx,
+                              const float* topk_weights, int64_t T, int H, int k, int E, int cap,
+                              void* recv, float* recv_scales, int32_t* recv_count,
+                              int32_t* recv_src_idx, float* recv_w, int32_t* token_slot,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    int s = check_routing(fn, topk_idx, T, k, E, 1);
+    if (s != EP_OK) return s;
+    if (cap < 1) return fail(EP_ERR_INVALID_ARGUMENT, "%s: capacity < 1", fn);
+    if (static_cast<int64_t>(E) * cap > INT32_MAX)
+        return fail(EP_ERR_UNSUPPORTED, "%s: num_experts * capacity >= 2^31", fn);
+    if (fp8 ? (H < 128 || H % 128 != 0) : (H < 8 || H % 8 != 0))
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: hidden must be a positive multiple of %d", fn,
+                    fp8 ? 128 : 8);
+    if (!recv_count) return fail(EP_ERR_INVALID_ARGUMENT, "%s: recv_count is NULL", fn);
+    if (T > 0 && (!x || !recv || !recv_src_idx || !token_slot || (fp8 && !recv_scales)))
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: a required pointer is NULL", fn);
+    if (T > 0 && (!aligned16(x) || !aligned16(recv) ||
+                  (fp8 && (reinterpret_cast<uintptr_t>(recv_scales) & 3u))))
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: misaligned x / receive buffer / scales", fn);
+    if (!fp8 && !ep::copy_launch_fits(T, H, k))
+        return fail(EP_ERR_UNSUPPORTED, "%s: num_tokens * hidden too large for one copy launch", fn);
+    const size_t need = ep::ll_workspace_bytes(T, k, E);
+    if (T > 0 && (!workspace || workspace_bytes < need))
+        return fail(EP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes", fn, need);
+    return hip_status(ep::launch_dispatch_ll(x, topk_idx, topk_weights, T, H, k, E, cap, recv,
+                                             fp8 ? recv_scales : nullptr, recv_count,
+                                             recv_src_idx, recv_w, token_slot, workspace,
+                                             static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+int ep_dispatch_ll(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                   int64_t num_tokens, int hidden, int num_topk, int num_experts, int capacity,
+                   void* recv_x, int32_t* recv_count, int32_t* recv_src_idx,
+                   float* recv_topk_weights, int32_t* token_slot, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    return dispatch_ll_common("ep_dispatch_ll", false, x, topk_idx, topk_weights, num_tokens, hidden,
+                              num_topk, num_experts, capacity, recv_x, nullptr, recv_count,
+                              recv_src_idx, recv_topk_weights, token_slot, workspace,
+                              workspace_bytes, stream);
+}
+
+int ep_dispatch_ll_fp8(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                       int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                       int capacity, uint8_t* recv_x_fp8, float* recv_scales,
+                       int32_t* recv_count, int32_t* recv_src_idx, float* recv_topk_weights,
+                       int32_t* token_slot, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    return dispatch_ll_common("ep_dispatch_ll_fp8", true, x, topk_idx, topk_weights, num_tokens,
+                              hidden, num_topk, num_experts, capacity, recv_x_fp8, recv_scales,
+                              recv_count, recv_src_idx, recv_topk_weights, token_slot, workspace,
+                              workspace_bytes, stream);
 }
 
 int ep_combine(const void* expert_out, int64_t num_rows, const int32_t* token_row,

@@ -54,17 +54,21 @@ constexpr int64_t kMaxLaunchThreads = 0xFFFFFFFFll;
 // row per wave); copy_launch_fits assumes it.
 constexpr int kCopyVec = 2;
 bool copy_launch_fits(int64_t T, int H, int fanout);
+// cap == 0: packed receive order (expert_offset / rank_offset written);
+// cap > 0: padded [E, cap] slots (recv_count written, token_row = slots).
 hipError_t launch_dispatch_small_bf16(const void* x, const int64_t* topk_idx,
                                       const float* topk_weights, int64_t T, int H, int k, int E,
-                                      int R, void* recv_x, int32_t* recv_src_idx, float* recv_w,
-                                      int32_t* expert_offset, int32_t* rank_offset,
-                                      int32_t* token_row, hipStream_t stream);
+                                      int R, int cap, void* recv_x, int32_t* recv_src_idx,
+                                      float* recv_w, int32_t* expert_offset, int32_t* rank_offset,
+                                      int32_t* recv_count, int32_t* token_row,
+                                      hipStream_t stream);
 hipError_t launch_dispatch_small_fp8(const void* x, const int64_t* topk_idx,
                                      const float* topk_weights, int64_t T, int H, int k, int E,
-                                     int R, uint8_t* recv_q, float* recv_scales,
+                                     int R, int cap, uint8_t* recv_q, float* recv_scales,
                                      int32_t* recv_src_idx, float* recv_w,
                                      int32_t* expert_offset, int32_t* rank_offset,
-                                     int32_t* token_row, hipStream_t stream);
+                                     int32_t* recv_count, int32_t* token_row,
+                                     hipStream_t stream);
 
 // ---- rank-deduplicated (high-throughput) dispatch -------------------------------
 size_t ht_workspace_bytes(int64_t T, int R);
@@ -72,6 +76,16 @@ hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const floa
                               int64_t T, int H, int k, int E, int R, void* recv_x,
                               int32_t* recv_src_idx, int64_t* recv_topk_idx, float* recv_w,
                               int32_t* rank_offset, int32_t* token_rank_row, void* workspace,
+                              hipStream_t stream);
+
+// ---- padded expert-major (low-latency) dispatch ----------------------------------
+size_t ll_workspace_bytes(int64_t T, int k, int E);
+// recv_q_or_x: bf16 rows [E*cap, H] when recv_scales is NULL, else FP8 codes
+// [E*cap, H] with scales [E*cap, H/128].
+hipError_t launch_dispatch_ll(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                              int64_t T, int H, int k, int E, int cap, void* recv_q_or_x,
+                              float* recv_scales, int32_t* recv_count, int32_t* recv_src_idx,
+                              float* recv_w, int32_t* token_slot, void* workspace,
                               hipStream_t stream);
 
 // ---- data movement ------------------------------------------------------------

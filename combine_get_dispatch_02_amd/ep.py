@@ -57,8 +57,13 @@ def lib() -> ctypes.CDLL:
     L.ep_dispatch_ht_workspace_bytes.restype = sz
     L.ep_dispatch_ht.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, sz, P]
     L.ep_dispatch_fp8_cached.argtypes = [P, P, i64, i32, i32, P, P, i64, P]
+    L.ep_dispatch_ll_workspace_bytes.argtypes = [i64, i32, i32]
+    L.ep_dispatch_ll_workspace_bytes.restype = sz
+    L.ep_dispatch_ll.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P, sz, P]
+    L.ep_dispatch_ll_fp8.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, sz, P]
     for f in ("ep_get_dispatch_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_combine",
-              "ep_dispatch_cached", "ep_dispatch_fp8_cached", "ep_dispatch_ht"):
+              "ep_dispatch_cached", "ep_dispatch_fp8_cached", "ep_dispatch_ht", "ep_dispatch_ll",
+              "ep_dispatch_ll_fp8"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -296,6 +301,71 @@ def ep_dispatch_ht(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: Option
             _ptr(out["token_rank_row"]), _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "ep_dispatch_ht")
     return out
+
+
+def ep_dispatch_ll_workspace_bytes(num_tokens: int, num_topk: int, num_experts: int) -> int:
+    return int(lib().ep_dispatch_ll_workspace_bytes(num_tokens, num_topk, num_experts))
+
+
+def _ll(fp8: bool, x, topk_idx, topk_weights, num_experts, capacity, out, workspace):
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    _need(topk_idx, "topk_idx", torch.int64, dev)
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32, dev)
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    E = num_experts
+    if topk_idx.shape[0] != T:
+        raise ValueError("x and topk_idx disagree on num_tokens")
+    if out is None:
+        out = dict(recv_count=torch.empty(E, dtype=torch.int32, device=dev),
+                   recv_src_idx=torch.empty((E, capacity), dtype=torch.int32, device=dev),
+                   recv_topk_weights=(torch.empty((E, capacity), dtype=torch.float32, device=dev)
+                                      if topk_weights is not None else None),
+                   token_slot=torch.empty((T, k), dtype=torch.int32, device=dev))
+        if fp8:
+            out["recv_x_fp8"] = torch.empty((E, capacity, H), dtype=torch.uint8, device=dev)
+            out["recv_scales"] = torch.empty((E, capacity, H // 128), dtype=torch.float32, device=dev)
+        else:
+            out["recv_x"] = torch.empty((E, capacity, H), dtype=torch.bfloat16, device=dev)
+    ws = _workspace(ep_dispatch_ll_workspace_bytes(T, k, E), dev, workspace)
+    L = lib()
+    with torch.cuda.device(dev):
+        if fp8:
+            st = L.ep_dispatch_ll_fp8(
+                _ptr(x), _ptr(topk_idx), _ptr(topk_weights), T, H, k, E, capacity,
+                _ptr(out["recv_x_fp8"]), _ptr(out["recv_scales"]), _ptr(out["recv_count"]),
+                _ptr(out["recv_src_idx"]), _ptr(out.get("recv_topk_weights")),
+                _ptr(out["token_slot"]), _ptr(ws), ws.numel(), _stream(dev))
+        else:
+            st = L.ep_dispatch_ll(
+                _ptr(x), _ptr(topk_idx), _ptr(topk_weights), T, H, k, E, capacity,
+                _ptr(out["recv_x"]), _ptr(out["recv_count"]), _ptr(out["recv_src_idx"]),
+                _ptr(out.get("recv_topk_weights")), _ptr(out["token_slot"]), _ptr(ws), ws.numel(),
+                _stream(dev))
+    _check(st, "ep_dispatch_ll_fp8" if fp8 else "ep_dispatch_ll")
+    return out
+
+
+def ep_dispatch_ll(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: Optional[torch.Tensor],
+                   num_experts: int, capacity: int, *,
+                   out: Optional[Dict[str, torch.Tensor]] = None,
+                   workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Padded expert-major dispatch: recv_x [E, capacity, H] (recv_count[e]
+    rows of expert e filled), recv_count [E], recv_src_idx [E, capacity],
+    recv_topk_weights [E, capacity], token_slot [T, k] (-1: empty or dropped).
+    Combine with ep_combine(y.view(E * capacity, H), token_slot, weights)."""
+    return _ll(False, x, topk_idx, topk_weights, num_experts, capacity, out, workspace)
+
+
+def ep_dispatch_ll_fp8(x: torch.Tensor, topk_idx: torch.Tensor,
+                       topk_weights: Optional[torch.Tensor], num_experts: int, capacity: int, *,
+                       out: Optional[Dict[str, torch.Tensor]] = None,
+                       workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """As ep_dispatch_ll with the FP8 cast of ep_dispatch_fp8: recv_x_fp8
+    [E, capacity, H] uint8 (E4M3FN codes) and recv_scales [E, capacity, H/128]."""
+    return _ll(True, x, topk_idx, topk_weights, num_experts, capacity, out, workspace)
 
 
 def ep_combine(expert_out: torch.Tensor, token_row: torch.Tensor,

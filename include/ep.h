@@ -227,6 +227,48 @@ int ep_dispatch_ht(const void* x, const int64_t* topk_idx, const float* topk_wei
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * ep_dispatch_ll / ep_dispatch_ll_fp8 -- padded expert-major ("low-latency")
+ * dispatch.  Page #852: the LL benchmark's receive buffer is one fixed-size
+ * region per expert (the commit that stops cloning that buffer inside the
+ * timed loop), and the low-latency runtime is tested at capacities 1 and 2.
+ * With one source the receive buffer is [E, capacity, H]; expert e owns rows
+ * e*capacity .. e*capacity + capacity - 1, filled in (token, slot) order, and
+ * a slot that finds its region full is dropped:
+ *
+ *   recv_x            [E, capacity, H]  bf16 out: slot = x[t], bit for bit
+ *     (ep_dispatch_ll_fp8: recv_x_fp8 [E, capacity, H] E4M3FN codes and
+ *      recv_scales [E, capacity, H/128] fp32, the cast of ep_dispatch_fp8)
+ *   recv_count        [E]          int32 out: min(slots routed to e, capacity)
+ *   recv_src_idx      [E, capacity] int32 out: source token of each filled slot
+ *   recv_topk_weights [E, capacity] fp32  out: topk_weights[t, j] of each
+ *                                     filled slot (may be NULL; ignored if
+ *                                     topk_weights is NULL)
+ *   token_slot        [T, k]       int32 out: e*capacity + position of (t, j),
+ *                                     or -1 (empty slot, or dropped)
+ *
+ * Rows recv_count[e] .. capacity-1 of each expert are not written.  Combine:
+ * ep_combine(expert_out [E*capacity, H], E*capacity, token_slot, weights, ...);
+ * a dropped slot then contributes nothing.  capacity = T never drops.
+ * Requires 1 <= capacity, E*capacity < 2^31, H % 8 == 0 (bf16) or
+ * H % 128 == 0 (FP8), the routing limits above (ranks are not involved) and
+ * (bf16) the copy-launch limit.  Workspace: ep_dispatch_ll_workspace_bytes.
+ * ------------------------------------------------------------------------- */
+size_t ep_dispatch_ll_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts);
+
+int ep_dispatch_ll(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                   int64_t num_tokens, int hidden, int num_topk, int num_experts, int capacity,
+                   void* recv_x, int32_t* recv_count, int32_t* recv_src_idx,
+                   float* recv_topk_weights, int32_t* token_slot, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+int ep_dispatch_ll_fp8(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                       int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                       int capacity, uint8_t* recv_x_fp8, float* recv_scales,
+                       int32_t* recv_count, int32_t* recv_src_idx, float* recv_topk_weights,
+                       int32_t* token_slot, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* ---------------------------------------------------------------------------
  * ep_combine -- gather each token's expert outputs back and sum them weighted
  * by topk_weights (intranode combine of "Scope / Intranode", consuming the
  * receiver-side map token_row that dispatch produced).  For every t, h:

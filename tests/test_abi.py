@@ -182,3 +182,42 @@ def test_copy_launch_limit_rejected_before_any_launch():
     assert _ht(**big) == EUNSUP
     st = ep.lib().ep_dispatch_cached(FAKE, FAKE, 2 ** 20, 8192, 8, FAKE, 2 ** 23, None)
     assert st == EUNSUP
+
+
+def _ll(fp8=False, **kw):
+    a = dict(x=FAKE, idx=FAKE, w=None, T=16, H=256, k=2, E=8, cap=4, recv=FAKE, scales=FAKE,
+             cnt=FAKE, src=FAKE, rw=None, slot=FAKE, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    L = ep.lib()
+    if fp8:
+        return L.ep_dispatch_ll_fp8(a["x"], a["idx"], a["w"], a["T"], a["H"], a["k"], a["E"], a["cap"],
+                                    a["recv"], a["scales"], a["cnt"], a["src"], a["rw"], a["slot"],
+                                    a["ws"], a["wsb"], None)
+    return L.ep_dispatch_ll(a["x"], a["idx"], a["w"], a["T"], a["H"], a["k"], a["E"], a["cap"],
+                            a["recv"], a["cnt"], a["src"], a["rw"], a["slot"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), EINVAL), (dict(k=0), EINVAL), (dict(k=65), EUNSUP), (dict(E=0), EINVAL),
+    (dict(E=4096), EUNSUP), (dict(cap=0), EINVAL), (dict(cap=-3), EINVAL),
+    (dict(E=2048, cap=2 ** 20), EUNSUP), (dict(H=12), EINVAL), (dict(H=0), EINVAL),
+    (dict(x=None), EINVAL), (dict(idx=None), EINVAL), (dict(recv=None), EINVAL),
+    (dict(cnt=None), EINVAL), (dict(cnt=None, T=0), EINVAL), (dict(src=None), EINVAL),
+    (dict(slot=None), EINVAL), (dict(x=ctypes.c_void_p(0x100008)), EINVAL),
+    (dict(recv=ctypes.c_void_p(0x100004)), EINVAL), (dict(wsb=16), EWS), (dict(ws=None), EWS),
+])
+def test_dispatch_ll_rejects(fp8, kw, code):
+    assert _ll(fp8=fp8, **kw) == code
+    assert ep.lib().ep_last_error().startswith(b"ep_dispatch_ll")
+
+
+@pytest.mark.parametrize("kw", [dict(H=264), dict(scales=None), dict(scales=ctypes.c_void_p(0x100002))])
+def test_dispatch_ll_fp8_specific_rejects(kw):
+    assert _ll(fp8=True, **kw) == EINVAL
+
+
+def test_dispatch_ll_copy_limit_and_workspace():
+    assert _ll(T=2 ** 20, H=8192, k=8, E=8, cap=8, wsb=1 << 40) == EUNSUP
+    assert ep.ep_dispatch_ll_workspace_bytes(4096, 8, 256) >= 2 * 4096 * 8 * 4
+    assert ep.ep_dispatch_ll_workspace_bytes(-1, 8, 256) == 0
