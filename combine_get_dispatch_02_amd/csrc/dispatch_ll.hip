@@ -82,7 +82,8 @@ hipError_t launch_dispatch_ll(const void* x, const int64_t* topk_idx, const floa
     int32_t* packed_src = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(token_row) + slots);
     int32_t* expert_offset = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(packed_src) + slots);
     hipError_t e = launch_dispatch_index(topk_idx, nullptr, T, k, E, 1, packed_src, nullptr,
-                                         expert_offset, nullptr, token_row, workspace, stream);
+                                         expert_offset, nullptr, token_row, workspace, x,
+                                         T * static_cast<int64_t>(H) * 2, stream);
     if (e != hipSuccess) return e;
     const int64_t n = T * k > E ? T * k : E;
     hipLaunchKernelGGL(ll_slots_kernel, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0,

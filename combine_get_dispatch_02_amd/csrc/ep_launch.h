@@ -37,10 +37,14 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R
 
 // ---- receive order (shared by both dispatch variants) -------------------------
 size_t index_workspace_bytes(int64_t T, int k, int E);
+// x / x_bytes (may be NULL / 0): the dispatched tokens, of which the one-launch
+// path reads up to 64 MB through the caches while it ranks (clobbering the
+// workspace's first 256 bytes), so the copy that follows finds them cached.
 hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weights, int64_t T,
                                  int k, int E, int R, int32_t* recv_src_idx, float* recv_w,
                                  int32_t* expert_offset, int32_t* rank_offset,
-                                 int32_t* token_row, void* workspace, hipStream_t stream);
+                                 int32_t* token_row, void* workspace, const void* x,
+                                 int64_t x_bytes, hipStream_t stream);
 
 // ---- small batches: receive order + copy in one launch -------------------------
 bool dispatch_is_small(int64_t T, int k);
