@@ -252,33 +252,8 @@ __global__ __launch_bounds__(kIndexThreads) void rows_kernel(
 // pf_vecs 16-byte vectors of x once through the caches while the tile blocks
 // rank: the index work uses a quarter of the CUs for ~12 us, and the copy
 // that follows then finds that part of x in the 256 MB Infinity Cache
-// instead of HBM (x is still read from HBM exactly once).  Their loads are
-// folded into one word per block, stored to pf_sink (scratch) so the loads
-// are kept.
+// instead of HBM (x is still read from HBM exactly once).
 constexpr int kFusedWeights = kMaxTileSlots / kFusedThreads;
-constexpr int kPrefetchBlocks = 192;
-constexpr int kPrefetchUnroll = 8;
-constexpr int64_t kPrefetchMaxBytes = int64_t(64) << 20;
-
-__device__ __forceinline__ void prefetch_x(const u32x4* __restrict__ src, int64_t nvec, int pf_block,
-                                           int pf_blocks, uint32_t* __restrict__ sink) {
-    uint32_t acc = 0;
-    const int64_t stride = static_cast<int64_t>(pf_blocks) * kFusedThreads;
-    int64_t i = static_cast<int64_t>(pf_block) * kFusedThreads + threadIdx.x;
-    for (; i + (kPrefetchUnroll - 1) * stride < nvec; i += kPrefetchUnroll * stride) {
-        u32x4 v[kPrefetchUnroll];
-#pragma unroll
-        for (int u = 0; u < kPrefetchUnroll; ++u) v[u] = src[i + u * stride];
-#pragma unroll
-        for (int u = 0; u < kPrefetchUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
-    }
-    for (; i < nvec; i += stride) {
-        const u32x4 v = src[i];
-        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
-    }
-    if (threadIdx.x == 0) sink[pf_block & 63] = acc;
-}
-
 __global__ __launch_bounds__(kFusedThreads) void rows_fused_kernel(
     const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int64_t T,
     int k, int E, int R, int tile_tokens, int nbits, int32_t* __restrict__ token_row,
@@ -286,8 +261,8 @@ __global__ __launch_bounds__(kFusedThreads) void rows_fused_kernel(
     int32_t* __restrict__ expert_offset, int32_t* __restrict__ rank_offset, int ntiles,
     const u32x4* __restrict__ pf_src, int64_t pf_vecs, uint32_t* __restrict__ pf_sink) {
     if (static_cast<int>(blockIdx.x) >= ntiles) {   // whole block: no tile work, no barrier
-        prefetch_x(pf_src, pf_vecs, static_cast<int>(blockIdx.x) - ntiles,
-                   static_cast<int>(gridDim.x) - ntiles, pf_sink);
+        prefetch_vectors<kFusedThreads>(pf_src, pf_vecs, static_cast<int>(blockIdx.x) - ntiles,
+                                        static_cast<int>(gridDim.x) - ntiles, pf_sink);
         return;
     }
     extern __shared__ int32_t lds[];
@@ -714,7 +689,7 @@ hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weig
         // Prefetch blocks only while that part of x fits the cache comfortably
         // (the workspace, at least 256 bytes, takes their 64 sink words).
         const int64_t pf_bytes = x ? (x_bytes < kPrefetchMaxBytes ? x_bytes : kPrefetchMaxBytes) : 0;
-        const int pf_blocks = pf_bytes > 0 ? kPrefetchBlocks : 0;
+        const int pf_blocks = pf_bytes > 0 ? prefetch_blocks(pf_bytes) : 0;
         hipLaunchKernelGGL(rows_fused_kernel, dim3(ntiles + pf_blocks), dim3(kFusedThreads), lds, stream,
                            topk_idx, w_in, T, k, E, R, tt, nbits, token_row, recv_src_idx, w_out,
                            expert_offset, rank_offset, ntiles, static_cast<const u32x4*>(x),

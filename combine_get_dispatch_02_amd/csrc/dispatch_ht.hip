@@ -7,7 +7,20 @@
 // receive buffer: one row per (token t, rank r) with t routed to r, ordered by
 // rank and then token.
 //
-// Four launches, deterministic, no global atomics:
+// Up to 16384 tokens, 16 ranks and top-16: two launches, deterministic, no
+// global atomics:
+//   ht_fused      one block of 1024 threads per 64-token tile: every block
+//                 sweeps all tokens' rank masks (ids loaded four tokens per
+//                 thread at a time) and counts, per rank, the tokens before
+//                 its tile and in all, with one ballot per rank per wave (no
+//                 atomics); a scan over ranks gives recv_rank_offset and the
+//                 tile's base rows; one wave ranks the tile's tokens by
+//                 ballots; token_rank_row and each row's source token and
+//                 remapped ids and weights are written from LDS, one token
+//                 per wave.  Extra blocks read x through the caches meanwhile
+//                 (see prefetch_vectors).
+//   copy          as below.
+// Otherwise four launches:
 //   ht_tile_hist  one token per thread, 256 tokens per tile: the token's rank
 //                 mask (R <= 64) from its k ids; per-tile, per-rank counts
 //   ht_rows       per tile: per-rank prefix over earlier tiles, a 64-lane scan
@@ -31,11 +44,17 @@ constexpr int kHtTile = 256;          // tokens per tile = threads per block
 constexpr int kHtWaves = kHtTile / kWave;
 constexpr int kHtHistBatch = 64;
 
+// Rank of a valid expert id (0 <= e < E <= 2048): a 32-bit division (a 64-bit
+// one is a long software sequence on this target).
+__device__ __forceinline__ int rank_of(int64_t e, int epr) {
+    return static_cast<int>(static_cast<uint32_t>(e) / static_cast<uint32_t>(epr));
+}
+
 __device__ __forceinline__ uint64_t rank_mask(const int64_t* __restrict__ ids, int k, int E, int epr) {
     uint64_t m = 0;
     for (int j = 0; j < k; ++j) {
         const int64_t e = ids[j];
-        if (e >= 0 && e < E) m |= uint64_t(1) << static_cast<int>(e / epr);
+        if (e >= 0 && e < E) m |= uint64_t(1) << rank_of(e, epr);
     }
     return m;
 }
@@ -146,11 +165,142 @@ __global__ __launch_bounds__(256) void ht_meta_kernel(
         const int64_t t = tr / R;
         const int r = static_cast<int>(tr - t * R);
         const int64_t e = topk_idx[t * k + j];
-        const bool local = e >= 0 && e < E && e / epr == r;
+        const bool local = e >= 0 && e < E && rank_of(e, epr) == r;
         recv_topk_idx[static_cast<int64_t>(row) * k + j] = local ? e - static_cast<int64_t>(r) * epr : -1;
         if (recv_w)
             recv_w[static_cast<int64_t>(row) * k + j] = (local && topk_weights) ? topk_weights[t * k + j] : 0.0f;
         if (j == 0) recv_src_idx[row] = static_cast<int32_t>(t);
+    }
+}
+
+constexpr int kHtFusedThreads = 1024;
+constexpr int kHtFusedWaves = kHtFusedThreads / kWave;
+constexpr int kHtFusedTile = kWave;                // tokens per tile: one ranking wave
+constexpr int kHtFusedMaxR = 16;
+constexpr int kHtFusedMaxK = 16;
+constexpr int64_t kHtFusedMaxTokens = 16384;
+
+// KMAX >= k slots per token; NQ tokens per thread per sweep step (KMAX * NQ
+// 64-bit ids in registers: 32 ids, 64 VGPRs).
+template <int KMAX, int NQ>
+__global__ __launch_bounds__(kHtFusedThreads) void ht_fused_kernel(
+    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int64_t T,
+    int k, int E, int R, int ntiles, int32_t* __restrict__ token_rank_row,
+    int32_t* __restrict__ recv_src_idx, int64_t* __restrict__ recv_topk_idx,
+    float* __restrict__ recv_w, int32_t* __restrict__ rank_offset, const u32x4* __restrict__ pf_src,
+    int64_t pf_vecs, uint32_t* __restrict__ pf_sink) {
+    if (static_cast<int>(blockIdx.x) >= ntiles) {   // whole block: no tile work, no barrier
+        prefetch_vectors<kHtFusedThreads>(pf_src, pf_vecs, static_cast<int>(blockIdx.x) - ntiles,
+                                          static_cast<int>(gridDim.x) - ntiles, pf_sink);
+        return;
+    }
+    __shared__ int32_t cnt_all[kHtFusedWaves][kHtFusedMaxR];
+    __shared__ int32_t cnt_pre[kHtFusedWaves][kHtFusedMaxR];
+    __shared__ int32_t tile_ids[kHtFusedTile * kHtFusedMaxK];   // -1 for an empty slot
+    __shared__ float tile_w[kHtFusedTile * kHtFusedMaxK];
+    __shared__ int32_t tile_row[kHtFusedTile * kHtFusedMaxR];
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int epr = E / R;
+    const int64_t lo = static_cast<int64_t>(blockIdx.x) * kHtFusedTile;
+    const int nt = static_cast<int>(T - lo < kHtFusedTile ? T - lo : kHtFusedTile);
+    const bool want_w = recv_w != nullptr && topk_weights != nullptr;
+
+    // The tile's weights are requested first, so they share the sweep's
+    // round trip (a load feeding an LDS store inside the sweep would wait on
+    // its own).
+    const int wsl = threadIdx.x;                  // kHtFusedTile * KMAX <= kHtFusedThreads
+    const float wreg = (want_w && wsl < nt * k) ? topk_weights[lo * k + wsl] : 0.0f;
+    // Sweep: lane r of every wave accumulates rank r's tokens (all / before the tile).
+    int my_all = 0, my_pre = 0;
+    for (int64_t t0 = 0; t0 < T; t0 += static_cast<int64_t>(NQ) * kHtFusedThreads) {
+        int64_t ids[NQ][KMAX];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int64_t t = t0 + q * kHtFusedThreads + threadIdx.x;
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j)
+                ids[q][j] = (t < T && j < k) ? topk_idx[t * k + j] : -1;
+        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int64_t t = t0 + q * kHtFusedThreads + threadIdx.x;
+            const bool in_tile = t >= lo && t < lo + nt;
+            uint32_t m = 0;
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) {
+                const int64_t e = ids[q][j];
+                const bool valid = j < k && e >= 0 && e < E;
+                if (valid) m |= 1u << rank_of(e, epr);
+                if (in_tile && j < k) tile_ids[(t - lo) * k + j] = valid ? static_cast<int32_t>(e) : -1;
+            }
+            for (int r = 0; r < R; ++r) {
+                const bool bit = (m >> r) & 1u;
+                const int a = __popcll(ballot(bit));
+                const int p = __popcll(ballot(bit && t < lo));
+                if (lane == r) {
+                    my_all += a;
+                    my_pre += p;
+                }
+            }
+        }
+    }
+    if (lane < R) {
+        cnt_all[wave][lane] = my_all;
+        cnt_pre[wave][lane] = my_pre;
+    }
+    if (want_w && wsl < nt * k) tile_w[wsl] = wreg;
+    __syncthreads();
+    if (wave == 0) {
+        // Lane r: rank r's tokens in all tiles and before this one; a scan
+        // over the lanes gives the ranks' first rows.
+        int tot = 0, pre = 0;
+        if (lane < R)
+            for (int w = 0; w < kHtFusedWaves; ++w) {
+                tot += cnt_all[w][lane];
+                pre += cnt_pre[w][lane];
+            }
+        int incl = tot;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int u = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += u;
+        }
+        const int base = incl - tot + pre;        // this tile's first row in rank `lane`
+        if (blockIdx.x == 0) {
+            if (lane < R) rank_offset[lane] = incl - tot;
+            if (lane == R - 1) rank_offset[R] = incl;
+        }
+        // Rank the tile's tokens: lane = token.
+        uint32_t m = 0;
+        if (lane < nt)
+            for (int j = 0; j < k; ++j) {
+                const int e = tile_ids[lane * k + j];
+                if (e >= 0) m |= 1u << rank_of(e, epr);
+            }
+        for (int r = 0; r < R; ++r) {
+            const uint64_t b = ballot((m >> r) & 1u);
+            const int row = read_lane(base, r) + __popcll(b & lanes_below());
+            if (lane < nt) tile_row[lane * R + r] = ((m >> r) & 1u) ? row : -1;
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nt * R; i += kHtFusedThreads) token_rank_row[lo * R + i] = tile_row[i];
+    // Per-row records: one token per wave, lanes over its (rank, slot) pairs,
+    // so a row's k ids and weights are contiguous stores.
+    const int per_token = R * k;
+    for (int tl = wave; tl < nt; tl += kHtFusedWaves) {
+        for (int c = lane; c < per_token; c += kWave) {
+            const int r = c / k;
+            const int j = c - r * k;
+            const int row = tile_row[tl * R + r];
+            if (row < 0) continue;
+            const int e = tile_ids[tl * k + j];
+            const bool local = e >= 0 && rank_of(e, epr) == r;
+            recv_topk_idx[static_cast<int64_t>(row) * k + j] = local ? e - r * epr : -1;
+            if (recv_w) recv_w[static_cast<int64_t>(row) * k + j] = (local && want_w) ? tile_w[tl * k + j] : 0.0f;
+            if (j == 0) recv_src_idx[row] = static_cast<int32_t>(lo + tl);
+        }
     }
 }
 
@@ -173,6 +323,25 @@ hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const floa
     if (T == 0) {
         hipLaunchKernelGGL(ht_zero_offsets_kernel, dim3(1), dim3(2 * kWave), 0, stream, rank_offset, R);
         return hipGetLastError();
+    }
+    if (T <= kHtFusedMaxTokens && R <= kHtFusedMaxR && k <= kHtFusedMaxK) {
+        const int ntiles = static_cast<int>(ceil_div(T, kHtFusedTile));
+        const int64_t x_bytes = T * static_cast<int64_t>(H) * 2;
+        const int64_t pf_bytes = x_bytes < kPrefetchMaxBytes ? x_bytes : kPrefetchMaxBytes;
+        const int pf_blocks = prefetch_blocks(pf_bytes);
+        if (k <= 8)
+            hipLaunchKernelGGL((ht_fused_kernel<8, 4>), dim3(ntiles + pf_blocks), dim3(kHtFusedThreads),
+                               0, stream, topk_idx, topk_weights, T, k, E, R, ntiles, token_rank_row,
+                               recv_src_idx, recv_topk_idx, recv_w, rank_offset,
+                               static_cast<const u32x4*>(x), pf_bytes / 16, static_cast<uint32_t*>(workspace));
+        else
+            hipLaunchKernelGGL((ht_fused_kernel<16, 2>), dim3(ntiles + pf_blocks), dim3(kHtFusedThreads),
+                               0, stream, topk_idx, topk_weights, T, k, E, R, ntiles, token_rank_row,
+                               recv_src_idx, recv_topk_idx, recv_w, rank_offset,
+                               static_cast<const u32x4*>(x), pf_bytes / 16, static_cast<uint32_t*>(workspace));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_dispatch_copy_bf16(x, token_rank_row, recv_x, T * R, T, H, R, stream);
     }
     const int ntiles = static_cast<int>(ceil_div(T, kHtTile));
     int32_t* hist = static_cast<int32_t*>(workspace);

@@ -81,4 +81,32 @@ __device__ __forceinline__ uint32_t e4m3fn_encode(float f) {
     return code | sign;
 }
 
+// Read src[0 .. nvec) once through the caches, as block pf_block of
+// pf_blocks blocks of NT threads (a grid-stride sweep, 8 loads in flight per
+// thread).  The values are folded into one word per block and stored to
+// sink[pf_block % 64] (scratch, >= 256 bytes) so the loads are kept.  Used by
+// index kernels to bring the tokens into the Infinity Cache while they rank,
+// ahead of the copy that reads them.
+template <int NT>
+__device__ __forceinline__ void prefetch_vectors(const u32x4* __restrict__ src, int64_t nvec,
+                                                 int pf_block, int pf_blocks,
+                                                 uint32_t* __restrict__ sink) {
+    constexpr int kUnroll = 8;
+    uint32_t acc = 0;
+    const int64_t stride = static_cast<int64_t>(pf_blocks) * NT;
+    int64_t i = static_cast<int64_t>(pf_block) * NT + threadIdx.x;
+    for (; i + (kUnroll - 1) * stride < nvec; i += kUnroll * stride) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    for (; i < nvec; i += stride) {
+        const u32x4 v = src[i];
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    if (threadIdx.x == 0) sink[pf_block & 63] = acc;
+}
+
 }  // namespace ep

@@ -25,9 +25,20 @@ constexpr size_t kFusedMaxLds = 64 * 1024;
 // Up to this many slots (T*k) each copy block derives its own token's rows and
 // ep_dispatch / ep_dispatch_fp8 are a single launch.
 constexpr int64_t kSmallSlots = 2048;
+// Index launches that run for ~10 us on part of the chip carry this many
+// extra blocks reading up to kPrefetchMaxBytes of x through the caches (well
+// inside the 256 MB Infinity Cache), for the copy that follows.
+constexpr int kPrefetchBlocks = 192;
+constexpr int64_t kPrefetchMaxBytes = int64_t(64) << 20;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
+// Prefetch blocks of 1024 threads (8 vectors each per step) for x_bytes of x.
+inline int prefetch_blocks(int64_t x_bytes) {
+    const int64_t bytes = x_bytes < kPrefetchMaxBytes ? x_bytes : kPrefetchMaxBytes;
+    const int64_t b = ceil_div(bytes / 16, 1024 * 8);
+    return static_cast<int>(b < kPrefetchBlocks ? b : kPrefetchBlocks);
+}
 
 // ---- layout -----------------------------------------------------------------
 size_t layout_workspace_bytes(int64_t T, int E, int R, int G);

@@ -47,7 +47,8 @@ __global__ __launch_bounds__(kLayoutTokensPerBlock) void layout_partial_kernel(
             const int64_t e = row[j];
             if (e >= 0 && e < E) {
                 atomicAdd(&h_e[e], 1);
-                m |= uint64_t(1) << static_cast<int>(e / epr);
+                // 0 <= e < E: a 32-bit division (64-bit is a long software sequence)
+                m |= uint64_t(1) << (static_cast<uint32_t>(e) / static_cast<uint32_t>(epr));
             }
         }
     }
