@@ -214,6 +214,46 @@ def graph_mode(args, wl, ep, torch, np, idxd, xd, wd, lay, ws_l, disp, ws_d, com
           flush=True)
 
 
+def drain_check(args, wl, ep, torch, np, idxd, xd, wd, disp, ws_d, comb, flush):
+    """Whether a timed phase leaves write-backs for later: each of ep_dispatch
+    and ep_combine is timed alone, then followed inside the same events by a
+    512 MiB read of unrelated memory, which is also timed alone.  If the
+    phase's stores were still in the caches at its end event, the read would
+    have to write them back and the pair would take longer than the two
+    parts."""
+    N = wl.T * wl.k
+    drain = torch.ones(64 << 20, dtype=torch.int64, device=xd.device)
+
+    def timed(fn):
+        ts = []
+        for i in range(args.warmup + args.steps):
+            flush(i)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            if i >= args.warmup:
+                ts.append(a.elapsed_time(b) * 1e3)
+        return float(np.median(ts))
+
+    def d():
+        ep.ep_dispatch(xd, idxd, wd, wl.E, wl.R, out=disp, workspace=ws_d)
+
+    def c():
+        ep.ep_combine(disp["recv_x"], disp["token_row"], wd, num_rows=N, out=comb)
+
+    r = timed(lambda: drain.sum())
+    res = {"mode": "drain_check", "workload": wl.describe(), "steps": args.steps,
+           "read_512MiB_us": round(r, 2)}
+    for name, fn in (("ep_dispatch", d), ("ep_combine", c)):
+        t1 = timed(fn)
+        t2 = timed(lambda: (fn(), drain.sum()))
+        res[name] = {"alone_us": round(t1, 2), "then_read_us": round(t2, 2),
+                     "deferred_us": round(t2 - r - t1, 2)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,6 +267,10 @@ def main():
                     help="instead of the headline: time one whole step (layout, dispatch, combine, "
                          "FP8 dispatch; no cache eviction) replayed from a captured HIP graph "
                          "against the same step launched eagerly")
+    ap.add_argument("--drain-check", action="store_true",
+                    help="instead of the headline: check that ep_dispatch and ep_combine leave no "
+                         "write-backs behind their end events (each timed alone and followed by "
+                         "a 512 MiB read)")
     ap.add_argument("--ll-capacity", type=int, default=0,
                     help="capacity (rows per expert) of the padded-layout phases; default: the "
                          "busiest expert's load rounded up to 64 rows")
@@ -356,6 +400,9 @@ def main():
 
     if args.graph:
         graph_mode(args, wl, ep, torch, np, idxd, xd, wd, lay, ws_l, disp, ws_d, comb, fp8)
+        return
+    if args.drain_check:
+        drain_check(args, wl, ep, torch, np, idxd, xd, wd, disp, ws_d, comb, flush)
         return
 
     for i in range(args.warmup):
