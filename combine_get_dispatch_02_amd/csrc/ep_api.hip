@@ -44,9 +44,18 @@ int check_routing(const char* fn, const int64_t* topk_idx, int64_t T, int k, int
     return EP_OK;
 }
 
+// The kernels keep 32-bit counters in the workspace.
+int check_workspace(const char* fn, int64_t T, const void* ws, size_t ws_bytes, size_t need) {
+    if (T > 0 && (!ws || ws_bytes < need))
+        return fail(EP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes", fn, need);
+    if (T > 0 && (reinterpret_cast<uintptr_t>(ws) & 3u))
+        return fail(EP_ERR_INVALID_ARGUMENT, "%s: workspace must be 4-byte aligned", fn);
+    return EP_OK;
+}
+
 int check_dispatch_common(const char* fn, const void* x, const int64_t* topk_idx, int64_t T,
                           int H, int k, int E, int R, const void* recv, const int32_t* recv_src_idx,
-                          const int32_t* expert_offset, const int32_t* token_row,
+                          const int32_t* expert_offset, const int32_t* token_row, const void* ws,
                           size_t ws_bytes) {
     int s = check_routing(fn, topk_idx, T, k, E, R);
     if (s != EP_OK) return s;
@@ -56,10 +65,7 @@ int check_dispatch_common(const char* fn, const void* x, const int64_t* topk_idx
         return fail(EP_ERR_INVALID_ARGUMENT, "%s: a required pointer is NULL", fn);
     if (T > 0 && (!aligned16(x) || !aligned16(recv)))
         return fail(EP_ERR_INVALID_ARGUMENT, "%s: x and the receive buffer must be 16-byte aligned", fn);
-    if (T > 0 && ws_bytes < ep::index_workspace_bytes(T, k, E))
-        return fail(EP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes", fn,
-                    ep::index_workspace_bytes(T, k, E));
-    return EP_OK;
+    return check_workspace(fn, T, ws, ws_bytes, ep::index_workspace_bytes(T, k, E));
 }
 
 }  // namespace
@@ -102,8 +108,8 @@ int ep_get_dispatch_layout(const int64_t* topk_idx, int64_t num_tokens, int num_
         return fail(EP_ERR_INVALID_ARGUMENT, "%s: a required pointer is NULL", fn);
     const size_t need = ep::layout_workspace_bytes(num_tokens, num_experts, num_ranks,
                                                    num_ranks / ranks_per_group);
-    if (num_tokens > 0 && (!workspace || workspace_bytes < need))
-        return fail(EP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes", fn, need);
+    s = check_workspace(fn, num_tokens, workspace, workspace_bytes, need);
+    if (s != EP_OK) return s;
     return hip_status(ep::launch_layout(topk_idx, num_tokens, num_topk, num_experts, num_ranks,
                                         ranks_per_group, num_tokens_per_rank,
                                         num_tokens_per_group, num_tokens_per_expert,
@@ -125,7 +131,7 @@ int ep_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weight
     const char* fn = "ep_dispatch";
     int s = check_dispatch_common(fn, x, topk_idx, num_tokens, hidden, num_topk, num_experts,
                                   num_ranks, recv_x, recv_src_idx, recv_expert_offset, token_row,
-                                  workspace ? workspace_bytes : 0);
+                                  workspace, workspace_bytes);
     if (s != EP_OK) return s;
     if (!ep::copy_launch_fits(num_tokens, hidden, num_topk))
         return fail(EP_ERR_UNSUPPORTED, "%s: num_tokens * hidden too large for one copy launch", fn);
@@ -159,7 +165,7 @@ int ep_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_we
     const char* fn = "ep_dispatch_fp8";
     int s = check_dispatch_common(fn, x, topk_idx, num_tokens, hidden, num_topk, num_experts,
                                   num_ranks, recv_x_fp8, recv_src_idx, recv_expert_offset,
-                                  token_row, workspace ? workspace_bytes : 0);
+                                  token_row, workspace, workspace_bytes);
     if (s != EP_OK) return s;
     if (hidden % 128 != 0) return fail(EP_ERR_INVALID_ARGUMENT, "%s: hidden %% 128 != 0", fn);
     if (num_tokens > 0 && !recv_scales)
@@ -259,8 +265,8 @@ int ep_dispatch_ht(const void* x, const int64_t* topk_idx, const float* topk_wei
     if (num_tokens > 0 && (!aligned16(x) || !aligned16(recv_x)))
         return fail(EP_ERR_INVALID_ARGUMENT, "%s: x and recv_x must be 16-byte aligned", fn);
     const size_t need = ep::ht_workspace_bytes(num_tokens, num_ranks);
-    if (num_tokens > 0 && (!workspace || workspace_bytes < need))
-        return fail(EP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes", fn, need);
+    s = check_workspace(fn, num_tokens, workspace, workspace_bytes, need);
+    if (s != EP_OK) return s;
     return hip_status(ep::launch_dispatch_ht(x, topk_idx, topk_weights, num_tokens, hidden, num_topk,
                                              num_experts, num_ranks, recv_x, recv_src_idx,
                                              recv_topk_idx, recv_topk_weights, recv_rank_offset,
@@ -295,8 +301,8 @@ static int dispatch_ll_common(const char* fn, bool fp8, const void* x, const int
     if (!fp8 && !ep::copy_launch_fits(T, H, k))
         return fail(EP_ERR_UNSUPPORTED, "%s: num_tokens * hidden too large for one copy launch", fn);
     const size_t need = ep::ll_workspace_bytes(T, k, E);
-    if (T > 0 && (!workspace || workspace_bytes < need))
-        return fail(EP_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes", fn, need);
+    s = check_workspace(fn, T, workspace, workspace_bytes, need);
+    if (s != EP_OK) return s;
     return hip_status(ep::launch_dispatch_ll(x, topk_idx, topk_weights, T, H, k, E, cap, recv,
                                              fp8 ? recv_scales : nullptr, recv_count,
                                              recv_src_idx, recv_w, token_slot, workspace,

@@ -22,8 +22,9 @@
  * device), row-major and densely packed, owned by the caller; the library
  * keeps no reference after the call returns and allocates nothing.  The
  * workspace is caller-owned device memory of at least the size reported by
- * the matching *_workspace_bytes() call; its contents on entry do not matter
- * and on exit are unspecified.
+ * the matching *_workspace_bytes() call, 4-byte aligned (the kernels keep
+ * 32-bit counters there; EP_ERR_INVALID_ARGUMENT otherwise); its contents on
+ * entry do not matter and on exit are unspecified.
  *
  * bf16 data is passed as raw 16-bit patterns (void*).
  *

@@ -221,3 +221,15 @@ def test_dispatch_ll_copy_limit_and_workspace():
     assert _ll(T=2 ** 20, H=8192, k=8, E=8, cap=8, wsb=1 << 40) == EUNSUP
     assert ep.ep_dispatch_ll_workspace_bytes(4096, 8, 256) >= 2 * 4096 * 8 * 4
     assert ep.ep_dispatch_ll_workspace_bytes(-1, 8, 256) == 0
+
+
+def test_misaligned_workspace_rejected():
+    """The kernels keep 32-bit counters in the workspace: a pointer that is not
+    4-byte aligned is rejected before anything is enqueued."""
+    odd = ctypes.c_void_p(0x100002)
+    assert _layout(ws=odd) == EINVAL
+    assert _dispatch(ws=odd) == EINVAL
+    assert _dispatch(fp8=True, ws=odd) == EINVAL
+    assert _ht(ws=odd) == EINVAL
+    assert _ll(ws=odd) == EINVAL
+    assert b"4-byte aligned" in ep.lib().ep_last_error()
