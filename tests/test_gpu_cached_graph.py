@@ -68,29 +68,52 @@ def test_cached_dispatch_skips_rows_out_of_range():
 
 @pytest.mark.parametrize("name", ["ll_fp8", "dsv3"])
 def test_whole_path_replays_in_hip_graph(name):
-    """layout -> dispatch -> combine -> FP8 dispatch captured once and replayed
-    with fresh activations and routing copied into the captured inputs; every
-    replay must equal the eager path on the same inputs, bit for bit, with
-    eager work and synchronisations between replays."""
+    """layout -> dispatch -> combine -> FP8 dispatch, then the rank-deduplicated
+    dispatch and its unweighted combine and the padded-layout dispatches (bf16
+    and FP8, capacity 4, so slots are dropped) and their combine, captured once
+    and replayed with fresh activations and routing copied into the captured
+    inputs; every replay must equal the eager path on the same inputs, bit for
+    bit, with eager work and synchronisations between replays."""
     wl = CONFIGS[name] if name == "ll_fp8" else CONFIGS[name].scaled(T=512)
     x, idx, w = make_workload(wl)
     xd, idxd, wd = dev_bf16(x), torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV)
+
+    cap = 4
 
     def step():
         lay = ep.ep_get_dispatch_layout(idxd, wl.E, wl.R, wl.P)
         d = ep.ep_dispatch(xd, idxd, wd, wl.E, wl.R)
         c = ep.ep_combine(d["recv_x"], d["token_row"], wd)
         f = ep.ep_dispatch_fp8(xd, idxd, wd, wl.E, wl.R)
-        return lay, d, c, f
+        h = ep.ep_dispatch_ht(xd, idxd, wd, wl.E, wl.R)
+        hc = ep.ep_combine(h["recv_x"], h["token_rank_row"], None)
+        ll = ep.ep_dispatch_ll(xd, idxd, wd, wl.E, cap)
+        lc = ep.ep_combine(ll["recv_x"].view(wl.E * cap, -1), ll["token_slot"], wd)
+        l8 = ep.ep_dispatch_ll_fp8(xd, idxd, wd, wl.E, cap)
+        return lay, d, c, f, h, hc, ll, lc, l8
 
     def flat(res):
-        lay, d, c, f = res
+        lay, d, c, f, h, hc, ll, lc, l8 = res
         out = [lay[k].view(torch.uint8).clone() for k in sorted(lay)]
         out += [d[k].view(torch.uint8).clone() for k in sorted(d) if d[k] is not None and k != "recv_x"]
         n = int(d["recv_expert_offset"][-1].item())
         out.append(d["recv_x"][:n].view(torch.uint8).clone())
         out.append(c.view(torch.uint8).clone())
         out += [f[k][:n].view(torch.uint8).clone() for k in ("recv_x_fp8", "recv_scales")]
+        nh = int(h["recv_rank_offset"][-1].item())
+        out += [h[k].view(torch.uint8).clone() for k in ("recv_rank_offset", "token_rank_row")]
+        out += [h[k][:nh].view(torch.uint8).clone()
+                for k in ("recv_x", "recv_src_idx", "recv_topk_idx", "recv_topk_weights")]
+        out.append(hc.view(torch.uint8).clone())
+        slots = ll["token_slot"].flatten()
+        slots = slots[slots >= 0].long()
+        for o in (ll, l8):
+            out += [o[k].view(torch.uint8).clone() for k in ("recv_count", "token_slot")]
+        out.append(ll["recv_x"].view(wl.E * cap, -1)[slots].view(torch.uint8).clone())
+        out.append(ll["recv_src_idx"].flatten()[slots].view(torch.uint8).clone())
+        out.append(l8["recv_x_fp8"].view(wl.E * cap, -1)[slots].clone())
+        out.append(l8["recv_scales"].view(wl.E * cap, -1)[slots].view(torch.uint8).clone())
+        out.append(lc.view(torch.uint8).clone())
         return out
 
     step()                                   # warm up allocator and kernels outside capture
