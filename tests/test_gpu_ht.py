@@ -115,8 +115,13 @@ def test_ht_parity_full_size(name):
     np.testing.assert_array_equal(got[toks], oracle.combine(rows_y, local, None))
 
 
+# One-launch index path (T <= 16384, R <= 16, k <= 16; top-k <= 8 and 9..16
+# instantiations) and the three-launch path beyond it, both sides of each limit.
 @pytest.mark.parametrize("T,k,E,R,H", [(1, 1, 1, 1, 8), (37, 3, 12, 6, 64), (300, 5, 24, 6, 136),
-                                       (700, 8, 2048, 64, 16), (257, 16, 64, 64, 64)])
+                                       (700, 8, 2048, 64, 16), (257, 16, 64, 64, 64),
+                                       (300, 12, 48, 12, 128), (130, 16, 16, 16, 64),
+                                       (200, 9, 34, 17, 64), (130, 17, 17, 1, 64),
+                                       (16384, 2, 64, 8, 16), (16385, 2, 64, 8, 16)])
 def test_ht_edge_shapes(T, k, E, R, H):
     rng = np.random.default_rng(T * R)
     idx = rng.integers(0, E, size=(T, k)).astype(np.int64)            # duplicates allowed
