@@ -95,6 +95,39 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, dev: Optional[torch.de
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_out(out: Dict[str, Optional[torch.Tensor]], dev: torch.device, spec) -> None:
+    """Caller-supplied outputs: spec rows are (name, shape, dtype, required,
+    capacity).  A capacity buffer needs at least shape[0] rows and exactly the
+    trailing shape; any other array needs exactly `shape`.  The kernels write
+    through raw pointers, so a smaller or mistyped tensor is refused here."""
+    for name, shape, dtype, required, capacity in spec:
+        t = out.get(name)
+        if t is None:
+            if required:
+                raise ValueError(f"out is missing {name}")
+            continue
+        _need(t, name, dtype, dev)
+        got = tuple(t.shape)
+        ok = (len(got) == len(shape) and got[0] >= shape[0] and got[1:] == tuple(shape[1:])) if capacity \
+            else got == tuple(shape)
+        if not ok:
+            want = f"[>= {shape[0]}{''.join(', ' + str(d) for d in shape[1:])}]" if capacity else str(list(shape))
+            raise ValueError(f"out[{name!r}] has shape {list(got)}, needs {want}")
+
+
+def _dispatch_spec(T, k, E, R, H, recv_name, recv_dtype, recv_cols, scales):
+    N = T * k
+    spec = [(recv_name, (N, recv_cols), recv_dtype, True, True),
+            ("recv_src_idx", (N,), torch.int32, True, True),
+            ("recv_topk_weights", (N,), torch.float32, False, True),
+            ("recv_expert_offset", (E + 1,), torch.int32, True, False),
+            ("recv_rank_offset", (R + 1,), torch.int32, False, False),
+            ("token_row", (T, k), torch.int32, True, False)]
+    if scales:
+        spec.append(("recv_scales", (N, H // 128), torch.float32, True, True))
+    return spec
+
+
 def ep_layout_workspace_bytes(num_tokens: int, num_experts: int, num_ranks: int,
                               ranks_per_group: int) -> int:
     return int(lib().ep_layout_workspace_bytes(num_tokens, num_experts, num_ranks, ranks_per_group))
@@ -132,6 +165,11 @@ def ep_get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: 
             num_tokens_per_expert=torch.empty(num_experts, dtype=torch.int32, device=dev),
             is_token_in_rank=torch.empty((T, num_ranks), dtype=torch.uint8, device=dev),
         )
+    else:
+        _check_out(out, dev, [("num_tokens_per_rank", (num_ranks,), torch.int32, True, False),
+                              ("num_tokens_per_group", (G,), torch.int32, False, False),
+                              ("num_tokens_per_expert", (num_experts,), torch.int32, True, False),
+                              ("is_token_in_rank", (T, num_ranks), torch.uint8, True, False)])
     ws = _workspace(ep_layout_workspace_bytes(T, num_experts, num_ranks, max(P, 1)), dev, workspace)
     with torch.cuda.device(dev):
         st = lib().ep_get_dispatch_layout(
@@ -173,6 +211,9 @@ def ep_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: Optional[
     if out is None:
         out = _dispatch_outputs(T, k, num_experts, num_ranks, dev, topk_weights is not None)
         out["recv_x"] = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    else:
+        _check_out(out, dev, _dispatch_spec(T, k, num_experts, num_ranks, H, "recv_x",
+                                            torch.bfloat16, H, False))
     ws = _workspace(ep_dispatch_workspace_bytes(T, k, num_experts), dev, workspace)
     with torch.cuda.device(dev):
         st = lib().ep_dispatch(
@@ -203,6 +244,9 @@ def ep_dispatch_fp8(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: Optio
         out = _dispatch_outputs(T, k, num_experts, num_ranks, dev, topk_weights is not None)
         out["recv_x_fp8"] = torch.empty((T * k, H), dtype=torch.uint8, device=dev)
         out["recv_scales"] = torch.empty((T * k, H // 128), dtype=torch.float32, device=dev)
+    else:
+        _check_out(out, dev, _dispatch_spec(T, k, num_experts, num_ranks, H, "recv_x_fp8",
+                                            torch.uint8, H, True))
     ws = _workspace(ep_dispatch_workspace_bytes(T, k, num_experts), dev, workspace)
     with torch.cuda.device(dev):
         st = lib().ep_dispatch_fp8(
@@ -254,6 +298,9 @@ def ep_dispatch_fp8_cached(x: torch.Tensor, token_row: torch.Tensor, recv_rows: 
     if out is None:
         out = dict(recv_x_fp8=torch.empty((recv_rows, H), dtype=torch.uint8, device=dev),
                    recv_scales=torch.empty((recv_rows, H // 128), dtype=torch.float32, device=dev))
+    else:
+        _check_out(out, dev, [("recv_x_fp8", (recv_rows, H), torch.uint8, True, True),
+                              ("recv_scales", (recv_rows, H // 128), torch.float32, True, True)])
     with torch.cuda.device(dev):
         st = lib().ep_dispatch_fp8_cached(_ptr(x), _ptr(token_row), T, H, k, _ptr(out["recv_x_fp8"]),
                                           _ptr(out["recv_scales"]), recv_rows, _stream(dev))
@@ -292,6 +339,14 @@ def ep_dispatch_ht(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: Option
                                       if topk_weights is not None else None),
                    recv_rank_offset=torch.empty(R + 1, dtype=torch.int32, device=dev),
                    token_rank_row=torch.empty((T, R), dtype=torch.int32, device=dev))
+    else:
+        cap = T * R
+        _check_out(out, dev, [("recv_x", (cap, H), torch.bfloat16, True, True),
+                              ("recv_src_idx", (cap,), torch.int32, True, True),
+                              ("recv_topk_idx", (cap, k), torch.int64, True, True),
+                              ("recv_topk_weights", (cap, k), torch.float32, False, True),
+                              ("recv_rank_offset", (R + 1,), torch.int32, True, False),
+                              ("token_rank_row", (T, R), torch.int32, True, False)])
     ws = _workspace(ep_dispatch_ht_workspace_bytes(T, R), dev, workspace)
     with torch.cuda.device(dev):
         st = lib().ep_dispatch_ht(
@@ -329,6 +384,17 @@ def _ll(fp8: bool, x, topk_idx, topk_weights, num_experts, capacity, out, worksp
             out["recv_scales"] = torch.empty((E, capacity, H // 128), dtype=torch.float32, device=dev)
         else:
             out["recv_x"] = torch.empty((E, capacity, H), dtype=torch.bfloat16, device=dev)
+    else:
+        spec = [("recv_count", (E,), torch.int32, True, False),
+                ("recv_src_idx", (E, capacity), torch.int32, True, False),
+                ("recv_topk_weights", (E, capacity), torch.float32, False, False),
+                ("token_slot", (T, k), torch.int32, True, False)]
+        if fp8:
+            spec += [("recv_x_fp8", (E, capacity, H), torch.uint8, True, False),
+                     ("recv_scales", (E, capacity, H // 128), torch.float32, True, False)]
+        else:
+            spec.append(("recv_x", (E, capacity, H), torch.bfloat16, True, False))
+        _check_out(out, dev, spec)
     ws = _workspace(ep_dispatch_ll_workspace_bytes(T, k, E), dev, workspace)
     L = lib()
     with torch.cuda.device(dev):
@@ -389,6 +455,8 @@ def ep_combine(expert_out: torch.Tensor, token_row: torch.Tensor,
         raise ValueError("num_rows exceeds expert_out rows")
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    else:
+        _check_out({"out": out}, dev, [("out", (T, H), torch.bfloat16, True, False)])
     with torch.cuda.device(dev):
         st = lib().ep_combine(_ptr(expert_out), rows, _ptr(token_row), _ptr(topk_weights), T, H,
                               k, _ptr(out), _stream(dev))

@@ -426,3 +426,32 @@ def test_combine_bit_exact_fma_chain(name):
         got = host_bits(ep.ep_combine(dev_bf16(y), torch.from_numpy(ref_d["token_row"]).to(DEV),
                                       torch.from_numpy(ww).to(DEV)))
         np.testing.assert_array_equal(got, ref_c)
+
+
+def test_binding_rejects_wrong_outputs():
+    """Caller-supplied outputs are checked before the raw pointers reach the
+    kernels: a smaller, mistyped or misplaced tensor raises, nothing runs."""
+    wl = CONFIGS["tiny"]
+    x, idx, w = make_workload(wl)
+    xd, idxd, wd = dev_bf16(x), torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV)
+    good = ep.ep_dispatch(xd, idxd, wd, wl.E, wl.R)
+    bad = dict(good, recv_x=good["recv_x"][:-1])                        # one row short
+    with pytest.raises(ValueError, match="recv_x"):
+        ep.ep_dispatch(xd, idxd, wd, wl.E, wl.R, out=bad)
+    bad = dict(good, token_row=good["token_row"].to(torch.int64))      # wrong dtype
+    with pytest.raises(TypeError, match="token_row"):
+        ep.ep_dispatch(xd, idxd, wd, wl.E, wl.R, out=bad)
+    with pytest.raises(ValueError, match="out"):
+        ep.ep_combine(good["recv_x"], good["token_row"], wd, out=torch.empty((wl.T, wl.H - 8), dtype=torch.bfloat16, device=DEV))
+    ll = ep.ep_dispatch_ll(xd, idxd, wd, wl.E, 4)
+    with pytest.raises(ValueError, match="needs"):
+        ep.ep_dispatch_ll(xd, idxd, wd, wl.E, 5, out=ll)                 # capacity changed
+    h = ep.ep_dispatch_ht(xd, idxd, wd, wl.E, wl.R)
+    with pytest.raises(ValueError, match="token_rank_row"):
+        ep.ep_dispatch_ht(xd, idxd, wd, wl.E, wl.R, out=dict(h, token_rank_row=h["token_rank_row"][:, :-1]))
+    with pytest.raises(ValueError, match="missing"):
+        ep.ep_dispatch_fp8(xd, idxd, wd, wl.E, wl.R, out={k_: v for k_, v in good.items() if k_ != "recv_x"})
+    # a larger capacity buffer is accepted
+    big = dict(good, recv_x=torch.empty((wl.T * wl.k + 5, wl.H), dtype=torch.bfloat16, device=DEV))
+    ep.ep_dispatch(xd, idxd, wd, wl.E, wl.R, out=big)
+    torch.cuda.synchronize()
