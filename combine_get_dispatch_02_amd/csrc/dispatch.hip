@@ -192,7 +192,13 @@ __global__ __launch_bounds__(kIndexThreads) void rows_kernel(
     int k, int E, int R, int tile_tokens, int ntiles, int nbits, const int32_t* __restrict__ hist,
     int32_t* __restrict__ token_row, int32_t* __restrict__ recv_src_idx,
     float* __restrict__ recv_w, int32_t* __restrict__ expert_offset,
-    int32_t* __restrict__ rank_offset) {
+    int32_t* __restrict__ rank_offset, const u32x4* __restrict__ pf_src, int64_t pf_vecs,
+    uint32_t* __restrict__ pf_sink) {
+    if (static_cast<int>(blockIdx.x) >= ntiles) {   // whole block: x prefetch only
+        prefetch_vectors<kIndexThreads>(pf_src, pf_vecs, static_cast<int>(blockIdx.x) - ntiles,
+                                        static_cast<int>(gridDim.x) - ntiles, pf_sink);
+        return;
+    }
     extern __shared__ int32_t lds[];
     int32_t* base = lds;
     int32_t* wc = lds + E;
@@ -661,11 +667,14 @@ static int index_tile_tokens(int64_t T, int k) {
     return static_cast<int>(tt < cap ? tt : cap);
 }
 
-size_t index_workspace_bytes(int64_t T, int k, int E) {
+// Workspace: the per-tile histograms of the two-launch path, then 256 bytes
+// where the x-prefetch blocks store their folded words.
+static size_t index_hist_bytes(int64_t T, int k, int E) {
     const int64_t ntiles = T > 0 ? ceil_div(T, index_tile_tokens(T, k)) : 0;
-    const size_t b = static_cast<size_t>(ntiles) * static_cast<size_t>(E) * sizeof(int32_t);
-    return round_up(b > 0 ? b : 1, 256);
+    return round_up(static_cast<size_t>(ntiles) * static_cast<size_t>(E) * sizeof(int32_t), 256);
 }
+
+size_t index_workspace_bytes(int64_t T, int k, int E) { return index_hist_bytes(T, k, E) + 256; }
 
 hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weights, int64_t T,
                                  int k, int E, int R, int32_t* recv_src_idx, float* recv_w,
@@ -682,27 +691,29 @@ hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weig
     const int nbits = E > 1 ? 32 - __builtin_clz(static_cast<unsigned>(E - 1)) : 0;
     const float* w_in = recv_w ? topk_weights : nullptr;
     float* w_out = topk_weights ? recv_w : nullptr;
+    const int64_t pf_bytes = x ? (x_bytes < kPrefetchMaxBytes ? x_bytes : kPrefetchMaxBytes) : 0;
+    uint32_t* pf_sink = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + index_hist_bytes(T, k, E));
     const size_t fused_lds = (static_cast<size_t>(2 + kIndexWaves) * E + kFusedThreads / kWave +
                               2 * static_cast<size_t>(tt) * k) * sizeof(int32_t);
     if (T * k <= kFusedMaxSlots && fused_lds <= kFusedMaxLds) {
         const size_t lds = fused_lds;
-        // Prefetch blocks only while that part of x fits the cache comfortably
-        // (the workspace, at least 256 bytes, takes their 64 sink words).
-        const int64_t pf_bytes = x ? (x_bytes < kPrefetchMaxBytes ? x_bytes : kPrefetchMaxBytes) : 0;
+        // Prefetch blocks only while that part of x fits the cache comfortably.
         const int pf_blocks = pf_bytes > 0 ? prefetch_blocks(pf_bytes) : 0;
         hipLaunchKernelGGL(rows_fused_kernel, dim3(ntiles + pf_blocks), dim3(kFusedThreads), lds, stream,
                            topk_idx, w_in, T, k, E, R, tt, nbits, token_row, recv_src_idx, w_out,
                            expert_offset, rank_offset, ntiles, static_cast<const u32x4*>(x),
-                           pf_bytes / 16, static_cast<uint32_t*>(workspace));
+                           pf_bytes / 16, pf_sink);
         return hipGetLastError();
     }
     int32_t* hist = static_cast<int32_t*>(workspace);
     hipLaunchKernelGGL(tile_hist_kernel, dim3(ntiles), dim3(kIndexThreads),
                        static_cast<size_t>(E) * sizeof(int32_t), stream, topk_idx, T, k, E, tt, hist);
     const size_t lds = (static_cast<size_t>(1 + kIndexWaves) * E + kIndexWaves) * sizeof(int32_t);
-    hipLaunchKernelGGL(rows_kernel, dim3(ntiles), dim3(kIndexThreads), lds, stream, topk_idx, w_in,
-                       T, k, E, R, tt, ntiles, nbits, hist, token_row, recv_src_idx, w_out,
-                       expert_offset, rank_offset);
+    // The ranking launch carries the x prefetch (in 256-thread blocks).
+    const int pf_blocks = pf_bytes > 0 ? 4 * prefetch_blocks(pf_bytes) : 0;
+    hipLaunchKernelGGL(rows_kernel, dim3(ntiles + pf_blocks), dim3(kIndexThreads), lds, stream, topk_idx,
+                       w_in, T, k, E, R, tt, ntiles, nbits, hist, token_row, recv_src_idx, w_out,
+                       expert_offset, rank_offset, static_cast<const u32x4*>(x), pf_bytes / 16, pf_sink);
     return hipGetLastError();
 }
 

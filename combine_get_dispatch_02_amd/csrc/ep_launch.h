@@ -19,8 +19,11 @@ constexpr int kMaxTiles = 64;
 constexpr int kMaxTileSlots = 4096;
 constexpr int kIndexThreads = 256;
 // Up to this many slots (T*k) one fused launch computes the receive order;
-// beyond it, a histogram launch feeds the ranking launch.
-constexpr int64_t kFusedMaxSlots = int64_t(1) << 18;
+// beyond it, a histogram launch feeds the ranking launch.  Every fused block
+// sweeps all T*k ids, so its cost grows with the batch: measured on MI355X
+// with the x prefetch on both paths, the two launches are as fast at 49152
+// slots and 27 us faster at 262144 (one ep_dispatch of 32768 x 7168, top-8).
+constexpr int64_t kFusedMaxSlots = int64_t(1) << 15;
 constexpr size_t kFusedMaxLds = 64 * 1024;
 // Up to this many slots (T*k) each copy block derives its own token's rows and
 // ep_dispatch / ep_dispatch_fp8 are a single launch.
@@ -48,9 +51,10 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R
 
 // ---- receive order (shared by both dispatch variants) -------------------------
 size_t index_workspace_bytes(int64_t T, int k, int E);
-// x / x_bytes (may be NULL / 0): the dispatched tokens, of which the one-launch
-// path reads up to 64 MB through the caches while it ranks (clobbering the
-// workspace's first 256 bytes), so the copy that follows finds them cached.
+// x / x_bytes (may be NULL / 0): the dispatched tokens, of which the ranking
+// launch reads up to 64 MB through the caches while it ranks (its folded
+// words go to the workspace's last 256 bytes), so the copy that follows finds
+// them cached.
 hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weights, int64_t T,
                                  int k, int E, int R, int32_t* recv_src_idx, float* recv_w,
                                  int32_t* expert_offset, int32_t* rank_offset,

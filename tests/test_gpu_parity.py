@@ -352,14 +352,17 @@ def test_edge_fp8_special_blocks():
 
 
 @pytest.mark.parametrize("T,k,E,R,H,mask", [
-    (40000, 8, 256, 8, 64, 0.0),      # T*k > 2^18: histogram launch + ranking launch
+    (40000, 8, 256, 8, 64, 0.0),      # T*k > 2^15: histogram launch + ranking launch
     (33000, 8, 64, 8, 64, 0.05),      # same path, masked slots, ragged last tile
     (3000, 6, 2048, 64, 128, 0.02),   # many experts and ranks (fused path, large LDS)
-    (20000, 16, 2048, 64, 16, 0.0),   # many experts, T*k > 2^18, k > 8
+    (20000, 16, 2048, 64, 16, 0.0),   # many experts, two launches, k > 8
+    (4096, 8, 256, 8, 64, 0.03),      # T*k = 2^15: the last fused size
+    (4097, 8, 256, 8, 64, 0.03),      # one token more: two launches
 ])
 def test_parity_receive_order_paths(T, k, E, R, H, mask):
-    """Both receive-order paths (one fused launch up to 2^18 slots, two
-    launches above) against the oracle, element by element."""
+    """Both receive-order paths (one fused launch up to 2^15 slots, two
+    launches above; both carry the x prefetch) against the oracle, element by
+    element."""
     _say(f"[parity-paths] T={T} k={k} E={E} R={R} H={H} mask={mask}")
     rng = np.random.default_rng(T + E)
     idx = np.argsort(rng.random((T, E), dtype=np.float32), axis=1)[:, :k].astype(np.int64)
