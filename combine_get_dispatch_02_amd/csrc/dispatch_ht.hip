@@ -10,8 +10,8 @@
 // Up to 16384 tokens, 16 ranks and top-16: two launches, deterministic, no
 // global atomics:
 //   ht_fused      one block of 1024 threads per 64-token tile: every block
-//                 sweeps all tokens' rank masks (ids loaded four tokens per
-//                 thread at a time) and counts, per rank, the tokens before
+//                 sweeps all tokens' rank masks (one token per thread per
+//                 step) and counts, per rank, the tokens before
 //                 its tile and in all, with one ballot per rank per wave (no
 //                 atomics); a scan over ranks gives recv_rank_offset and the
 //                 tile's base rows; one wave ranks the tile's tokens by
@@ -180,8 +180,11 @@ constexpr int kHtFusedMaxR = 16;
 constexpr int kHtFusedMaxK = 16;
 constexpr int64_t kHtFusedMaxTokens = 16384;
 
-// KMAX >= k slots per token; NQ tokens per thread per sweep step (KMAX * NQ
-// 64-bit ids in registers: 32 ids, 64 VGPRs).
+// KMAX >= k slots per token; NQ tokens per thread per sweep step.  One token
+// per step is fastest on MI355X even where it takes four steps (4096
+// tokens): 19.9 us against 22.4 us with four tokens (and 10.9 against 17.7
+// us at 128 tokens), the larger unrolled id arrays costing more than the
+// extra round trips.
 template <int KMAX, int NQ>
 __global__ __launch_bounds__(kHtFusedThreads) void ht_fused_kernel(
     const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int64_t T,
@@ -330,12 +333,12 @@ hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const floa
         const int64_t pf_bytes = x_bytes < kPrefetchMaxBytes ? x_bytes : kPrefetchMaxBytes;
         const int pf_blocks = prefetch_blocks(pf_bytes);
         if (k <= 8)
-            hipLaunchKernelGGL((ht_fused_kernel<8, 4>), dim3(ntiles + pf_blocks), dim3(kHtFusedThreads),
+            hipLaunchKernelGGL((ht_fused_kernel<8, 1>), dim3(ntiles + pf_blocks), dim3(kHtFusedThreads),
                                0, stream, topk_idx, topk_weights, T, k, E, R, ntiles, token_rank_row,
                                recv_src_idx, recv_topk_idx, recv_w, rank_offset,
                                static_cast<const u32x4*>(x), pf_bytes / 16, static_cast<uint32_t*>(workspace));
         else
-            hipLaunchKernelGGL((ht_fused_kernel<16, 2>), dim3(ntiles + pf_blocks), dim3(kHtFusedThreads),
+            hipLaunchKernelGGL((ht_fused_kernel<16, 1>), dim3(ntiles + pf_blocks), dim3(kHtFusedThreads),
                                0, stream, topk_idx, topk_weights, T, k, E, R, ntiles, token_rank_row,
                                recv_src_idx, recv_topk_idx, recv_w, rank_offset,
                                static_cast<const u32x4*>(x), pf_bytes / 16, static_cast<uint32_t*>(workspace));
