@@ -36,7 +36,10 @@ constexpr int kHistBatch = 64;
 constexpr int kSlotsPerLane = kMaxTileSlots / kIndexThreads;
 // Fused receive-order kernel: every block histograms all T*k slots itself.
 constexpr int kFusedThreads = 1024;
-constexpr int kFusedBatch = 32;   // slots per thread per sweep step (loads in flight)
+// Slots per thread per sweep step (loads in flight).  8 measured ~1 us faster
+// per ep_dispatch than 32 at 4096 x 8 slots, despite four round trips instead
+// of one: the smaller unrolled batch costs less.
+constexpr int kFusedBatch = 8;
 
 // Per-tile expert histogram: hist[tile][e] = valid slots of the tile's tokens
 // routed to e (LDS atomics; integer sums do not depend on order).
