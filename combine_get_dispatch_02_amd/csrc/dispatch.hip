@@ -125,13 +125,16 @@ __device__ __forceinline__ void load_tile_slots(const int64_t* __restrict__ topk
 // 64 slots at a time, in order: a slot's row = its wave's cursor for the
 // expert + the number of lower lanes with the same expert (wave64 ballot
 // matching); the highest such lane then advances the cursor (LDS accesses of
-// one wave complete in program order).  Called by every thread of the block.
+// one wave complete in program order).  With cap > 0 (padded layout) base[e]
+// holds positions within expert e instead of rows, and a slot's row becomes
+// e*cap + position, or -1 from position cap on.  Called by every thread of the
+// block.
 __device__ __forceinline__ void rank_tile(const int (&ids)[kSlotsPerLane],
                                           const float (&wt)[kSlotsPerLane], const int32_t* base,
                                           int32_t* wc, int E, int S, int Q, int64_t s0, int64_t t0,
                                           int k, int nbits, int32_t* __restrict__ token_row,
                                           int32_t* __restrict__ recv_src_idx,
-                                          float* __restrict__ recv_w) {
+                                          float* __restrict__ recv_w, int cap) {
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
     const bool ranker = threadIdx.x < kIndexThreads;
@@ -165,10 +168,11 @@ __device__ __forceinline__ void rank_tile(const int (&ids)[kSlotsPerLane],
         int row = -1;
         if (valid) row = my[e] + __popcll(peers & lanes_below());
         if (valid && (peers >> lane) == 1) my[e] += __popcll(peers);
+        if (cap > 0 && row >= 0) row = row < cap ? e * cap + row : -1;   // padded slot
         if (in) {
             const int64_t gs = s0 + s;
             token_row[gs] = row;
-            if (valid) {
+            if (row >= 0) {
                 recv_src_idx[row] = static_cast<int32_t>(t0) +
                                     static_cast<int32_t>(static_cast<unsigned>(s) / static_cast<unsigned>(k));
                 if (recv_w) recv_w[row] = wt[i];
@@ -195,8 +199,8 @@ __global__ __launch_bounds__(kIndexThreads) void rows_kernel(
     int k, int E, int R, int tile_tokens, int ntiles, int nbits, const int32_t* __restrict__ hist,
     int32_t* __restrict__ token_row, int32_t* __restrict__ recv_src_idx,
     float* __restrict__ recv_w, int32_t* __restrict__ expert_offset,
-    int32_t* __restrict__ rank_offset, const u32x4* __restrict__ pf_src, int64_t pf_vecs,
-    uint32_t* __restrict__ pf_sink) {
+    int32_t* __restrict__ rank_offset, int cap, int32_t* __restrict__ recv_count,
+    const u32x4* __restrict__ pf_src, int64_t pf_vecs, uint32_t* __restrict__ pf_sink) {
     if (static_cast<int>(blockIdx.x) >= ntiles) {   // whole block: x prefetch only
         prefetch_vectors<kIndexThreads>(pf_src, pf_vecs, static_cast<int>(blockIdx.x) - ntiles,
                                         static_cast<int>(gridDim.x) - ntiles, pf_sink);
@@ -239,11 +243,18 @@ __global__ __launch_bounds__(kIndexThreads) void rows_kernel(
     for (int i = 0; i < kSlotsPerLane; ++i)
         ids[i] = (raw[i] >= 0 && raw[i] < E) ? static_cast<int>(raw[i]) : -1;
     __syncthreads();
-    const int total = block_exclusive_scan<kIndexThreads>(base, E, wave_tot);
-    if (c == 0) write_offsets(base, total, E, R, expert_offset, rank_offset);
-    for (int e = threadIdx.x; e < E; e += kIndexThreads) base[e] += wc[e];
+    if (cap > 0) {        // padded layout: counts, and positions within each expert
+        for (int e = threadIdx.x; e < E; e += kIndexThreads) {
+            if (c == 0) recv_count[e] = min(base[e], cap);
+            base[e] = wc[e];
+        }
+    } else {
+        const int total = block_exclusive_scan<kIndexThreads>(base, E, wave_tot);
+        if (c == 0) write_offsets(base, total, E, R, expert_offset, rank_offset);
+        for (int e = threadIdx.x; e < E; e += kIndexThreads) base[e] += wc[e];
+    }
     __syncthreads();
-    rank_tile(ids, wt, base, wc, E, S, Q, s0, t0, k, nbits, token_row, recv_src_idx, recv_w);
+    rank_tile(ids, wt, base, wc, E, S, Q, s0, t0, k, nbits, token_row, recv_src_idx, recv_w, cap);
 }
 
 // Fused path (one launch): one block of kFusedThreads per tile.  Every block
@@ -267,8 +278,9 @@ __global__ __launch_bounds__(kFusedThreads) void rows_fused_kernel(
     const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int64_t T,
     int k, int E, int R, int tile_tokens, int nbits, int32_t* __restrict__ token_row,
     int32_t* __restrict__ recv_src_idx, float* __restrict__ recv_w,
-    int32_t* __restrict__ expert_offset, int32_t* __restrict__ rank_offset, int ntiles,
-    const u32x4* __restrict__ pf_src, int64_t pf_vecs, uint32_t* __restrict__ pf_sink) {
+    int32_t* __restrict__ expert_offset, int32_t* __restrict__ rank_offset, int ntiles, int cap,
+    int32_t* __restrict__ recv_count, const u32x4* __restrict__ pf_src, int64_t pf_vecs,
+    uint32_t* __restrict__ pf_sink) {
     if (static_cast<int>(blockIdx.x) >= ntiles) {   // whole block: no tile work, no barrier
         prefetch_vectors<kFusedThreads>(pf_src, pf_vecs, static_cast<int>(blockIdx.x) - ntiles,
                                         static_cast<int>(gridDim.x) - ntiles, pf_sink);
@@ -331,9 +343,14 @@ __global__ __launch_bounds__(kFusedThreads) void rows_fused_kernel(
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kFusedThreads) rest[e] += pre[e];
     __syncthreads();
-    const int total = block_exclusive_scan<kFusedThreads>(rest, E, wave_tot);
-    if (c == 0) write_offsets(rest, total, E, R, expert_offset, rank_offset);
-    for (int e = threadIdx.x; e < E; e += kFusedThreads) pre[e] += rest[e];
+    if (cap > 0) {        // padded layout: counts; pre already holds positions
+        if (c == 0)
+            for (int e = threadIdx.x; e < E; e += kFusedThreads) recv_count[e] = min(rest[e], cap);
+    } else {
+        const int total = block_exclusive_scan<kFusedThreads>(rest, E, wave_tot);
+        if (c == 0) write_offsets(rest, total, E, R, expert_offset, rank_offset);
+        for (int e = threadIdx.x; e < E; e += kFusedThreads) pre[e] += rest[e];
+    }
     // The ranking waves pick up their slots from LDS.
     int ids[kSlotsPerLane];
     float wt[kSlotsPerLane];
@@ -350,7 +367,7 @@ __global__ __launch_bounds__(kFusedThreads) void rows_fused_kernel(
         }
     }
     __syncthreads();
-    rank_tile(ids, wt, pre, wc, E, S, Q, s0, t0, k, nbits, token_row, recv_src_idx, recv_w);
+    rank_tile(ids, wt, pre, wc, E, S, Q, s0, t0, k, nbits, token_row, recv_src_idx, recv_w, cap);
 }
 
 __global__ void zero_offsets_kernel(int32_t* expert_offset, int E, int32_t* rank_offset, int R) {
@@ -683,7 +700,7 @@ hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weig
                                  int k, int E, int R, int32_t* recv_src_idx, float* recv_w,
                                  int32_t* expert_offset, int32_t* rank_offset,
                                  int32_t* token_row, void* workspace, const void* x,
-                                 int64_t x_bytes, hipStream_t stream) {
+                                 int64_t x_bytes, int cap, int32_t* recv_count, hipStream_t stream) {
     if (T == 0) {
         hipLaunchKernelGGL(zero_offsets_kernel, dim3(1), dim3(256), 0, stream, expert_offset, E,
                            rank_offset, R);
@@ -704,8 +721,8 @@ hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weig
         const int pf_blocks = pf_bytes > 0 ? prefetch_blocks(pf_bytes) : 0;
         hipLaunchKernelGGL(rows_fused_kernel, dim3(ntiles + pf_blocks), dim3(kFusedThreads), lds, stream,
                            topk_idx, w_in, T, k, E, R, tt, nbits, token_row, recv_src_idx, w_out,
-                           expert_offset, rank_offset, ntiles, static_cast<const u32x4*>(x),
-                           pf_bytes / 16, pf_sink);
+                           expert_offset, rank_offset, ntiles, cap, recv_count,
+                           static_cast<const u32x4*>(x), pf_bytes / 16, pf_sink);
         return hipGetLastError();
     }
     int32_t* hist = static_cast<int32_t*>(workspace);
@@ -716,7 +733,8 @@ hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weig
     const int pf_blocks = pf_bytes > 0 ? 4 * prefetch_blocks(pf_bytes) : 0;
     hipLaunchKernelGGL(rows_kernel, dim3(ntiles + pf_blocks), dim3(kIndexThreads), lds, stream, topk_idx,
                        w_in, T, k, E, R, tt, ntiles, nbits, hist, token_row, recv_src_idx, w_out,
-                       expert_offset, rank_offset, static_cast<const u32x4*>(x), pf_bytes / 16, pf_sink);
+                       expert_offset, rank_offset, cap, recv_count, static_cast<const u32x4*>(x),
+                       pf_bytes / 16, pf_sink);
     return hipGetLastError();
 }
 

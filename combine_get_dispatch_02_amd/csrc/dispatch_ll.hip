@@ -11,38 +11,15 @@
 //
 // T*k <= 2048: one launch -- the small-batch dispatch kernels rank each
 // token's slots in-block and write the padded slots directly.
-// Larger batches: the receive-order kernels of ep_dispatch run into the
-// workspace (token_row, expert offsets), ll_slots turns each packed row into
-// its padded slot (position = row - expert_offset[e]), and the copy kernels of
-// ep_dispatch fill the slots, skipping dropped ones.
+// Larger batches: the receive-order kernels of ep_dispatch in their padded
+// mode (a slot's position within its expert, without the expert offset,
+// becomes e*cap + position, or -1 from cap on; block 0 writes the counts),
+// then the copy kernels of ep_dispatch fill the slots, skipping dropped ones.
 #include "ep_device.h"
 #include "ep_launch.h"
 
 namespace ep {
 namespace {
-
-__global__ __launch_bounds__(256) void ll_slots_kernel(
-    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights,
-    const int32_t* __restrict__ token_row, const int32_t* __restrict__ expert_offset, int64_t T,
-    int k, int E, int cap, int32_t* __restrict__ token_slot, int32_t* __restrict__ recv_src_idx,
-    float* __restrict__ recv_w, int32_t* __restrict__ recv_count) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i < T * k) {
-        const int row = token_row[i];
-        int slot = -1;
-        if (row >= 0) {   // row >= 0 only for a valid id
-            const int e = static_cast<int>(topk_idx[i]);
-            const int pos = row - expert_offset[e];
-            if (pos < cap) slot = e * cap + pos;
-        }
-        token_slot[i] = slot;
-        if (slot >= 0) {
-            recv_src_idx[slot] = static_cast<int32_t>(i / k);
-            if (recv_w) recv_w[slot] = topk_weights[i];
-        }
-    }
-    if (i < E) recv_count[i] = min(expert_offset[i + 1] - expert_offset[i], cap);
-}
 
 __global__ void ll_zero_counts_kernel(int32_t* __restrict__ recv_count, int E) {
     for (int e = threadIdx.x; e < E; e += blockDim.x) recv_count[e] = 0;
@@ -50,11 +27,7 @@ __global__ void ll_zero_counts_kernel(int32_t* __restrict__ recv_count, int E) {
 
 }  // namespace
 
-size_t ll_workspace_bytes(int64_t T, int k, int E) {
-    const size_t slots = round_up(static_cast<size_t>(T) * static_cast<size_t>(k) * sizeof(int32_t), 256);
-    return round_up(index_workspace_bytes(T, k, E), 256) + 2 * slots +
-           round_up((static_cast<size_t>(E) + 1) * sizeof(int32_t), 256);
-}
+size_t ll_workspace_bytes(int64_t T, int k, int E) { return index_workspace_bytes(T, k, E); }
 
 hipError_t launch_dispatch_ll(const void* x, const int64_t* topk_idx, const float* topk_weights,
                               int64_t T, int H, int k, int E, int cap, void* recv_q_or_x,
@@ -76,20 +49,10 @@ hipError_t launch_dispatch_ll(const void* x, const int64_t* topk_idx, const floa
                                           recv_src_idx, recv_w, nullptr, nullptr, recv_count,
                                           token_slot, stream);
     }
-    char* ws = static_cast<char*>(workspace);
-    const size_t slots = round_up(static_cast<size_t>(T) * static_cast<size_t>(k) * sizeof(int32_t), 256);
-    int32_t* token_row = reinterpret_cast<int32_t*>(ws + round_up(index_workspace_bytes(T, k, E), 256));
-    int32_t* packed_src = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(token_row) + slots);
-    int32_t* expert_offset = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(packed_src) + slots);
-    hipError_t e = launch_dispatch_index(topk_idx, nullptr, T, k, E, 1, packed_src, nullptr,
-                                         expert_offset, nullptr, token_row, workspace, x,
-                                         T * static_cast<int64_t>(H) * 2, stream);
-    if (e != hipSuccess) return e;
-    const int64_t n = T * k > E ? T * k : E;
-    hipLaunchKernelGGL(ll_slots_kernel, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0,
-                       stream, topk_idx, topk_weights, token_row, expert_offset, T, k, E, cap,
-                       token_slot, recv_src_idx, (topk_weights ? recv_w : nullptr), recv_count);
-    e = hipGetLastError();
+    const hipError_t e = launch_dispatch_index(topk_idx, topk_weights, T, k, E, 1, recv_src_idx,
+                                               recv_w, nullptr, nullptr, token_slot, workspace, x,
+                                               T * static_cast<int64_t>(H) * 2, cap, recv_count,
+                                               stream);
     if (e != hipSuccess) return e;
     const int64_t rows = static_cast<int64_t>(E) * cap;
     if (fp8)

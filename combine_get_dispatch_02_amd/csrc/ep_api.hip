@@ -147,7 +147,8 @@ int ep_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weight
                                              num_experts, num_ranks, recv_src_idx,
                                              recv_topk_weights, recv_expert_offset,
                                              recv_rank_offset, token_row, workspace, x,
-                                             num_tokens * static_cast<int64_t>(hidden) * 2, st),
+                                             num_tokens * static_cast<int64_t>(hidden) * 2, 0,
+                                             nullptr, st),
                    fn);
     if (s != EP_OK) return s;
     return hip_status(ep::launch_dispatch_copy_bf16(x, token_row, recv_x, num_tokens * num_topk,
@@ -184,7 +185,8 @@ int ep_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_we
                                              num_experts, num_ranks, recv_src_idx,
                                              recv_topk_weights, recv_expert_offset,
                                              recv_rank_offset, token_row, workspace, x,
-                                             num_tokens * static_cast<int64_t>(hidden) * 2, st),
+                                             num_tokens * static_cast<int64_t>(hidden) * 2, 0,
+                                             nullptr, st),
                    fn);
     if (s != EP_OK) return s;
     return hip_status(ep::launch_dispatch_copy_fp8(x, token_row, recv_x_fp8, recv_scales,

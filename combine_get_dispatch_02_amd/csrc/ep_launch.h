@@ -55,11 +55,14 @@ size_t index_workspace_bytes(int64_t T, int k, int E);
 // launch reads up to 64 MB through the caches while it ranks (its folded
 // words go to the workspace's last 256 bytes), so the copy that follows finds
 // them cached.
+// cap == 0: packed receive order (expert_offset / rank_offset written);
+// cap > 0: padded [E, cap] slots (token_row holds slots, recv_count written,
+// recv_src_idx / recv_w indexed by slot).
 hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weights, int64_t T,
                                  int k, int E, int R, int32_t* recv_src_idx, float* recv_w,
                                  int32_t* expert_offset, int32_t* rank_offset,
                                  int32_t* token_row, void* workspace, const void* x,
-                                 int64_t x_bytes, hipStream_t stream);
+                                 int64_t x_bytes, int cap, int32_t* recv_count, hipStream_t stream);
 
 // ---- small batches: receive order + copy in one launch -------------------------
 bool dispatch_is_small(int64_t T, int k);
