@@ -135,8 +135,13 @@ def cpu_baseline(wl, x, idx, w, budget_s):
     roff = np.empty(R + 1, np.int32)
     trow = np.empty((T, k), np.int32)
     out = np.empty((T, H), np.uint16)
+    G = wl.G
+    per_rank = np.empty(R, np.int32)
+    per_group = np.empty(G, np.int32)
+    per_expert = np.empty(E, np.int32)
+    in_rank = np.empty((T, R), np.uint8)
     p = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
-    t_d = t_c = 0.0
+    t_d = t_c = t_l = 0.0
     passes = 0
     t_start = time.perf_counter()
     while passes == 0 or time.perf_counter() - t_start < budget_s:
@@ -146,11 +151,29 @@ def cpu_baseline(wl, x, idx, w, budget_s):
         t1 = time.perf_counter()
         rc |= L.oracle_combine(p(recv), N, p(trow), p(w), T, H, k, p(out))
         t2 = time.perf_counter()
+        rc |= L.oracle_layout(p(idx), T, k, E, R, wl.P, p(per_rank), p(per_group), p(per_expert),
+                              p(in_rank))
+        t3 = time.perf_counter()
         if rc:
             raise RuntimeError("oracle failed")
         t_d += t1 - t0
         t_c += t2 - t1
+        t_l += t3 - t2
         passes += 1
+    # The FP8 oracle encodes by a search over the code table: timed on the
+    # first 64 tokens only and reported per token.
+    ts = min(T, 64)
+    ns = ts * k
+    q8 = np.empty((ns, H), np.uint8)
+    s8 = np.empty((ns, H // 128), np.float32)
+    src8, rw8 = np.empty(ns, np.int32), np.empty(ns, np.float32)
+    eoff8, roff8, trow8 = np.empty(E + 1, np.int32), np.empty(R + 1, np.int32), np.empty((ts, k), np.int32)
+    x8, idx8, w8 = (np.ascontiguousarray(a[:ts]) for a in (x, idx, w))
+    t4 = time.perf_counter()
+    if L.oracle_dispatch_fp8(p(x8), p(idx8), p(w8), ts, H, k, E, R, p(q8), p(s8), p(src8), p(rw8),
+                             p(eoff8), p(roff8), p(trow8)):
+        raise RuntimeError("oracle failed")
+    fp8_us_per_token = 1e6 * (time.perf_counter() - t4) / ts
     b = algorithmic_bytes(wl)
     gbs = (b["dispatch"] + b["combine"]) * passes / (t_d + t_c) / 1e9
     try:
@@ -162,10 +185,13 @@ def cpu_baseline(wl, x, idx, w, budget_s):
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"{wl.describe()}: {passes} full passes of oracle dispatch + combine "
+        "sample": (f"{wl.describe()}: {passes} full passes of oracle dispatch + combine (+ layout) "
                    f"(identity experts), {t_d + t_c:.1f} s, 1 thread"),
         "dispatch_ms": round(1e3 * t_d / passes, 2),
         "combine_ms": round(1e3 * t_c / passes, 2),
+        "layout_ms": round(1e3 * t_l / passes, 3),
+        "dispatch_fp8_us_per_token": round(fp8_us_per_token, 1),
+        "dispatch_fp8_note": f"timed on the first {ts} tokens (the FP8 oracle searches the code table)",
         "host_cores_available": len(os.sched_getaffinity(0)),
         "host_cpu": model,
     }
@@ -423,6 +449,20 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # Secondary: the same dispatch and combine with warm caches (no eviction).
+    warm_ev = []
+    for i in range(max(args.steps // 5, 5)):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        ep.ep_dispatch(xd, idxd, wd, E, R, out=disp, workspace=ws_d)
+        e[1].record()
+        ep.ep_combine(disp["recv_x"], disp["token_row"], wd, num_rows=N, out=comb)
+        e[2].record()
+        warm_ev.append(e)
+    torch.cuda.synchronize()
+    warm_d = np.array([e[0].elapsed_time(e[1]) for e in warm_ev[1:]]) * 1e3
+    warm_c = np.array([e[1].elapsed_time(e[2]) for e in warm_ev[1:]]) * 1e3
+
     if args.calibration_copy:
         cal_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         cal_dst = torch.empty_like(cal_src)
@@ -454,10 +494,24 @@ def main():
     c_us = float(ms["combine"].mean()) * 1e3
     achieved = B["combine"] / (c_us * 1e-6) / 1e9
     traffic = load_traffic(B["combine"])
-    roofline = {"kernel": "combine_kernel (ep_combine)", "bound": "hbm",
+    # An event pair with nothing between it, after the same eviction: the part
+    # of every phase time that is the events' own cost, not the kernel's.
+    empty = []
+    for i in range(20):
+        flush(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        b.record()
+        torch.cuda.synchronize()
+        empty.append(a.elapsed_time(b) * 1e3)
+    pair_us = float(np.median(empty))
+    roofline = {"kernel": "combine_kernel<2, 8, true> (ep_combine)", "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "alg_bytes_per_launch": int(B["combine"]), "avg_launch_us": round(c_us, 2)}
+                "alg_bytes_per_launch": int(B["combine"]), "avg_launch_us": round(c_us, 2),
+                "empty_event_pair_us": round(pair_us, 2),
+                "note": "avg_launch_us is the HIP-event time of the one-kernel ep_combine call, so it "
+                        "includes one event pair; the kernel-trace average is lower by about that"}
 
     cpu = None
     if not args.skip_cpu_baseline:
@@ -483,6 +537,12 @@ def main():
         "caches_flushed_between_phases": not args.no_flush,
         "wall_ms_per_step_incl_flush": round(1e3 * wall / args.steps, 4),
         "phases": phase_info,
+        "warm": {"dispatch_us": round(float(np.median(warm_d)), 2),
+                 "combine_us": round(float(np.median(warm_c)), 2),
+                 "value": round((B["dispatch"] + B["combine"]) /
+                                ((np.median(warm_d) + np.median(warm_c)) * 1e-6) / 1e9, 1),
+                 "note": "secondary: dispatch then combine back to back, no cache eviction "
+                         "(x and part of the rows may be served from the 256 MB Infinity Cache)"},
         "rank_dedup": {"rows": n_ht, "rows_per_token": round(n_ht / max(T, 1), 4),
                        "dispatch_plus_combine_GBps": round(ht_gbs, 1),
                        "pct_of_hbm_peak": round(100 * ht_gbs / HBM_PEAK_GBS, 2),
