@@ -4,13 +4,13 @@
 One step is one pass of the whole hot path over one batch of synthetic
 input already resident in HBM:
     ep_get_dispatch_layout -> ep_dispatch -> ep_combine -> ep_dispatch_fp8
-with the combine fed the dispatched rows (identity experts), followed by the
-rank-deduplicated pair ep_dispatch_ht -> ep_combine (unweighted, over the
-per-rank rows) and the padded expert-major (low-latency) layout
-ep_dispatch_ll -> ep_combine (over the slot map) -> ep_dispatch_ll_fp8, with
-the capacity set to the busiest expert's load rounded up to 64 rows (nothing
-dropped), all reported
-as extra phases beside the headline.  Before each
+with the combine fed the dispatched rows (identity experts).  Extra phases,
+reported beside the headline and not part of it: the rank-deduplicated pair
+ep_dispatch_ht -> ep_combine (unweighted, over the per-rank rows), the padded
+expert-major (low-latency) layout ep_dispatch_ll -> ep_combine (over the slot
+map) -> ep_dispatch_ll_fp8 with the capacity set to the busiest expert's load
+rounded up to 64 rows (nothing dropped), and ep_dispatch_cached (the copy
+kernel alone, reusing token_row).  Before each
 phase (outside its events) a 512 MiB write followed by a 512 MiB read of
 another buffer evicts L2 and the 256 MB Infinity Cache: the phase's inputs
 are then only in HBM and the caches hold clean, unrelated lines, so no
@@ -88,6 +88,8 @@ def algorithmic_bytes(wl, n_ht=None, n_ll=None):
         dispatch=reads + 2 * T * H + 2 * N * H + maps,
         dispatch_fp8=reads + 2 * T * H + N * H + 4 * N * (H // 128) + maps,
         combine=4 * T * k + 4 * T * k + 2 * N * H + 2 * T * H,
+        # the copy alone, driven by a saved token_row (x read, rows written, map read)
+        dispatch_cached=2 * T * H + 2 * N * H + 4 * T * k,
         dispatch_ht=8 * T * k + 4 * T * k + 2 * T * H + 2 * n * H + ht_maps,
         combine_ht=4 * T * R + 2 * n * H + 2 * T * H,
         # padded layout, m slots kept: token_slot, src and weight per kept
@@ -374,11 +376,12 @@ def main():
                token_slot=torch.empty((T, k), dtype=torch.int32, device=dev))
     ws_ll = torch.empty(ep.ep_dispatch_ll_workspace_bytes(T, k, E), dtype=torch.uint8, device=dev)
     comb_ll = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    cached = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
     flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     flush_src = torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
 
     phases = ["layout", "dispatch", "combine", "dispatch_fp8", "dispatch_ht", "combine_ht",
-              "dispatch_ll", "combine_ll", "dispatch_ll_fp8"]
+              "dispatch_ll", "combine_ll", "dispatch_ll_fp8", "dispatch_cached"]
 
     def flush(i):
         if not args.no_flush:
@@ -420,9 +423,13 @@ def main():
         ev[15].record()
         ep.ep_dispatch_ll_fp8(xd, idxd, wd, E, cap_ll, out=ll8, workspace=ws_ll)
         ev[16].record()
+        flush(i + 8)
+        ev[17].record()
+        ep.ep_dispatch_cached(xd, disp["token_row"], N, out=cached)
+        ev[18].record()
 
     def events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(17)]
+        return [torch.cuda.Event(enable_timing=True) for _ in range(19)]
 
     if args.graph:
         graph_mode(args, wl, ep, torch, np, idxd, xd, wd, lay, ws_l, disp, ws_d, comb, fp8)
@@ -473,7 +480,7 @@ def main():
 
     ms = {p: np.array([e[a].elapsed_time(e[b]) for e in evs])
           for p, (a, b) in zip(phases, [(0, 1), (1, 2), (3, 4), (5, 6), (7, 8), (9, 10), (11, 12),
-                                        (13, 14), (15, 16)])}
+                                        (13, 14), (15, 16), (17, 18)])}
     B = algorithmic_bytes(wl, n_ht, n_ll)
     t_dc = float(ms["dispatch"].sum() + ms["combine"].sum()) / 1e3
     value = (B["dispatch"] + B["combine"]) * args.steps / t_dc / 1e9
@@ -505,6 +512,12 @@ def main():
         torch.cuda.synchronize()
         empty.append(a.elapsed_time(b) * 1e3)
     pair_us = float(np.median(empty))
+    k_us = float(ms["dispatch_cached"].mean()) * 1e3
+    k_gbs = B["dispatch_cached"] / (k_us * 1e-6) / 1e9
+    roofline_copy = {"kernel": "copy_bf16_kernel (ep_dispatch_cached: the dispatch copy alone, "
+                               "x read from HBM)", "bound": "hbm", "achieved": round(k_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+                     "alg_bytes_per_launch": int(B["dispatch_cached"]), "avg_launch_us": round(k_us, 2)}
     roofline = {"kernel": "combine_kernel<2, 8, true> (ep_combine)", "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -557,6 +570,7 @@ def main():
                               "expert's load rounded up to 64 rows (nothing dropped); not part of "
                               "value or ms_per_step"},
         "roofline": roofline,
+        "roofline_dispatch_copy": roofline_copy,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
