@@ -121,7 +121,8 @@ def test_ht_parity_full_size(name):
                                        (700, 8, 2048, 64, 16), (257, 16, 64, 64, 64),
                                        (300, 12, 48, 12, 128), (130, 16, 16, 16, 64),
                                        (200, 9, 34, 17, 64), (130, 17, 17, 1, 64),
-                                       (16384, 2, 64, 8, 16), (16385, 2, 64, 8, 16)])
+                                       (16384, 2, 64, 8, 16), (16385, 2, 64, 8, 16),
+                                       (100, 64, 128, 8, 64), (90, 64, 2048, 64, 16)])
 def test_ht_edge_shapes(T, k, E, R, H):
     rng = np.random.default_rng(T * R)
     idx = rng.integers(0, E, size=(T, k)).astype(np.int64)            # duplicates allowed

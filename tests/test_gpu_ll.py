@@ -106,7 +106,8 @@ def test_ll_two_kernel_index_path(T, k, E, cap, H):
 
 
 @pytest.mark.parametrize("T,k,E,cap,H", [(1, 1, 1, 1, 128), (37, 3, 12, 2, 128), (9, 16, 8, 5, 256),
-                                         (700, 8, 2048, 3, 128)])
+                                         (700, 8, 2048, 3, 128), (30, 64, 128, 3, 128),
+                                         (100, 64, 2048, 2, 128)])
 def test_ll_edge_shapes(T, k, E, cap, H):
     rng = np.random.default_rng(T * k + cap)
     idx = rng.integers(0, E, size=(T, k)).astype(np.int64)          # duplicates allowed

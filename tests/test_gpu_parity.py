@@ -288,7 +288,10 @@ def test_edge_duplicates_and_out_of_range_ids():
                                        (257, 8, 64, 64, 64), (1000, 3, 2048, 64, 16),
                                        (100, 16, 64, 8, 136),     # single-launch path, k > 8
                                        (256, 8, 256, 8, 64),      # exactly 2048 slots
-                                       (257, 8, 256, 8, 64)])     # one token past it
+                                       (257, 8, 256, 8, 64),      # one token past it
+                                       (20, 64, 64, 4, 64),       # top-64 (the limit), one launch
+                                       (40, 64, 128, 8, 64),      # top-64, fused receive order
+                                       (600, 64, 2048, 64, 16)])  # top-64, 2048 experts, 64 ranks, two launches
 def test_edge_degenerate_shapes(T, k, E, R, H):
     rng = np.random.default_rng(T + k)
     idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int64)
