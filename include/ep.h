@@ -74,7 +74,8 @@ typedef enum {
 #define EP_MAX_TOPK 64          /* num_topk                                   */
 #define EP_MAX_RANKS 64         /* num_ranks                                  */
 #define EP_MAX_EXPERTS 2048     /* num_experts                                */
-/* The bf16 copies (ep_dispatch, ep_dispatch_cached, ep_dispatch_ht) run in one
+/* The bf16 copies (ep_dispatch, ep_dispatch_cached, ep_dispatch_ht,
+ * ep_dispatch_ll) run in one
  * launch of T * ceil(H / 1024) blocks of 64 * min(fanout, 8) threads, where
  * fanout is num_topk (num_ranks for ep_dispatch_ht); a launch holds at most
  * 2^32 - 1 threads, and larger shapes return EP_ERR_UNSUPPORTED before any
