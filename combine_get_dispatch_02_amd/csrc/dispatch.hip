@@ -422,6 +422,10 @@ __global__ __launch_bounds__(512) void copy_bf16_kernel(const u32x4* __restrict_
 // vectors) as part of a 128-channel block shared by 8 aligned lanes: block
 // amax by three xor-shuffles, scale = amax / 448 (one correctly rounded fp32
 // division), codes = E4M3FN(x / scale), or all zero when the scale is 0.
+// amax is the largest magnitude that is not NaN: magnitudes are compared as
+// integers (the order of non-negative floats, +inf included), with NaN bit
+// patterns counted as 0, so the result does not depend on how a float max
+// treats quiet or signalling NaNs.
 // Every lane of the wave must call it (the shuffles span the wave).
 __device__ __forceinline__ u32x4 quantize16(u32x4 a0, u32x4 a1, float& scale) {
     float f[16];
@@ -432,13 +436,16 @@ __device__ __forceinline__ u32x4 quantize16(u32x4 a0, u32x4 a1, float& scale) {
         f[8 + 2 * i] = bf16_lo(a1[i]);
         f[8 + 2 * i + 1] = bf16_hi(a1[i]);
     }
-    float amax = 0.0f;
+    uint32_t amax = 0u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
-    amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
-    const float s = amax / 448.0f;
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t m = __float_as_uint(f[i]) & 0x7FFFFFFFu;
+        amax = max(amax, m > 0x7F800000u ? 0u : m);
+    }
+    amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 1, kWave)));
+    amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 2, kWave)));
+    amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 4, kWave)));
+    const float s = __uint_as_float(amax) / 448.0f;
     u32x4 q = {0u, 0u, 0u, 0u};
     if (s > 0.0f) {
 #pragma unroll

@@ -62,15 +62,15 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 // value.  Normal range (|f| >= 2^-6): round the fp32 mantissa to 3 bits and
 // rebias the exponent from 127 to 7.  Below 2^-6 the codes are the multiples
 // of 2^-9, so the code is |f| * 512 rounded to an integer (0..8; 8 is the
-// smallest normal, code 0x08).
+// smallest normal, code 0x08).  Every NaN, whatever its sign and payload,
+// becomes 0x7F, so the code does not depend on how a division propagated it.
 __device__ __forceinline__ uint32_t e4m3fn_encode(float f) {
     const uint32_t u = __float_as_uint(f);
     const uint32_t sign = (u >> 24) & 0x80u;
     const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return 0x7Fu;                         // NaN
     uint32_t code;
-    if (a > 0x7F800000u) {
-        code = 0x7Fu;                                          // NaN
-    } else if (a >= 0x43E00000u) {                             // >= 448.0f, inf
+    if (a >= 0x43E00000u) {                                    // >= 448.0f, inf
         code = 0x7Eu;
     } else if (a >= 0x3C800000u) {                             // >= 2^-6
         const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);

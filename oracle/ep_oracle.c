@@ -256,9 +256,12 @@ int oracle_dispatch(const uint16_t* x, const int64_t* topk_idx, const float* top
  * dispatch with kUseFP8).  For block c of token t (the page gives no
  * arithmetic; this is the plainest one: a true division by the scale, and an
  * all-zero block gets scale 0 and zero codes):
- *   a = max |x| over the block's 128 channels (in fp32; bf16 -> fp32 is exact)
+ *   a = max |x| over the block's 128 channels that are not NaN (in fp32;
+ *       bf16 -> fp32 is exact; NaN fails the comparison and is passed over)
  *   s = a / 448                       (one IEEE fp32 division)
  *   q = E4M3(x / s)   if s > 0, else all codes 0x00
+ * so a NaN channel gets the NaN code 0x7F when s > 0, and an infinite a gives
+ * s = inf (finite channels -> signed zero, infinite ones inf/inf = NaN).
  * H must be a multiple of 128. */
 int oracle_quantize_row(const uint16_t* xrow, int H, uint8_t* q, float* scales)
 {

@@ -20,7 +20,7 @@ import torch
 
 import oracle
 from combine_get_dispatch_02_amd import ep
-from combine_get_dispatch_02_amd.workloads import CONFIGS, expert_outputs, make_workload, mask_slots
+from combine_get_dispatch_02_amd.workloads import CONFIGS, expert_outputs, make_workload, mask_slots, random_bf16
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -352,6 +352,72 @@ def test_edge_fp8_special_blocks():
     np.testing.assert_array_equal(q, ref["recv_x_fp8"][:N])
     r2 = ref["token_row"][2, 0]
     assert 0 < s[r2, 0] < np.finfo(np.float32).tiny          # denormal scale survived
+
+
+def non_finite_x(rng, T, H):
+    """bf16 tokens with NaNs (both signs, quiet and signalling), infinities,
+    blocks whose only non-zero entry is a NaN, and bf16's largest finite value."""
+    x = random_bf16(rng, T, H)
+    specials = np.array([0x7FC0, 0xFFC0, 0x7F81, 0xFF81, 0x7F80, 0xFF80, 0x7F7F, 0xFF7F], np.uint16)
+    hit = rng.random((T, H)) < 0.01
+    x[hit] = rng.choice(specials, size=int(hit.sum()))
+    for t in range(0, T, 7):
+        b = 128 * int(rng.integers(0, H // 128))
+        x[t, b:b + 128] = 0
+        x[t, b + int(rng.integers(0, 128))] = rng.choice(specials[:4])
+    return x
+
+
+@pytest.mark.parametrize("T,k", [(40, 4), (300, 8)], ids=["one-launch", "index+copy"])
+def test_edge_non_finite_tokens(T, k):
+    """Non-finite activations through every FP8 entry point (codes and scales
+    bit-exact: NaN-free amax, any NaN -> 0x7F), the bf16 dispatch (bits carried
+    as they are) and the combine (NaN where the oracle has NaN, every other
+    output bit-exact)."""
+    E, R, H = 64, 8, 1024
+    rng = np.random.default_rng(T + k)
+    x = non_finite_x(rng, T, H)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int64)
+    w = rng.random((T, k)).astype(np.float32)
+    print(f"[non-finite] T={T} k={k} E={E} H={H}", flush=True)
+    xd, idxd, wd = dev_bf16(x), torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV)
+
+    ref = oracle.dispatch_fp8(x, idx, w, E, R)
+    N = int(ref["recv_expert_offset"][-1])
+    f = ep.ep_dispatch_fp8(xd, idxd, wd, E, R, out=prefilled_dispatch_out(T, k, H, E, R, True))
+    c = ep.ep_dispatch_fp8_cached(xd, f["token_row"], N)
+    torch.cuda.synchronize()
+    check_index_maps(f, ref, N)
+    for o in (f, c):
+        sc = o["recv_scales"].cpu().numpy()[:N]
+        np.testing.assert_array_equal(sc.view(np.uint32), ref["recv_scales"][:N].view(np.uint32))
+        np.testing.assert_array_equal(o["recv_x_fp8"].cpu().numpy()[:N], ref["recv_x_fp8"][:N])
+    assert np.any(np.isinf(ref["recv_scales"][:N])) and np.any(ref["recv_scales"][:N] == 0)
+
+    cap = 3
+    lref = oracle.dispatch_ll_fp8(x, idx, w, E, cap)
+    ll = ep.ep_dispatch_ll_fp8(xd, idxd, wd, E, cap)
+    torch.cuda.synchronize()
+    filled = lref["recv_src_idx"] >= 0
+    np.testing.assert_array_equal(ll["recv_x_fp8"].cpu().numpy()[filled], lref["recv_x_fp8"][filled])
+    np.testing.assert_array_equal(ll["recv_scales"].cpu().numpy()[filled].view(np.uint32),
+                                  lref["recv_scales"][filled].view(np.uint32))
+
+    bref = oracle.dispatch(x, idx, w, E, R)
+    d = ep.ep_dispatch(xd, idxd, wd, E, R)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_bits(d["recv_x"])[:N], bref["recv_x"][:N])
+
+    y = non_finite_x(rng, N, H)
+    for wt in (w, None):
+        exp = oracle.combine(y, ref["token_row"], wt)
+        got = host_bits(ep.ep_combine(dev_bf16(y), f["token_row"],
+                                      None if wt is None else torch.from_numpy(wt).to(DEV)))
+        nan_exp = (exp & 0x7FFF) > 0x7F80
+        nan_got = (got & 0x7FFF) > 0x7F80
+        np.testing.assert_array_equal(nan_got, nan_exp)
+        assert nan_exp.any()
+        np.testing.assert_array_equal(got[~nan_exp], exp[~nan_exp])
 
 
 @pytest.mark.parametrize("T,k,E,R,H,mask", [

@@ -142,6 +142,31 @@ def test_tiny_amax_keeps_denormal_scale():
     assert q[5] == 0x7E and q[6] == 0xFE
 
 
+def test_non_finite_blocks():
+    """Non-finite activations (the page defines none; the reading kept is plain
+    IEEE arithmetic on a NaN-free amax): NaN never raises or poisons the block
+    amax; every NaN, of either sign, quiet or signalling, encodes as 0x7F when
+    the block scale is positive; an infinite amax gives an infinite scale, so
+    finite channels become signed zeros and the infinities NaN (inf / inf)."""
+    x = np.zeros(512, np.uint16)
+    one, two, three, five = 0x3F80, 0x4000, 0x4040, 0x40A0
+    x[0], x[1] = one, two
+    x[2], x[3], x[4], x[5] = 0x7FC0, 0xFFC0, 0x7F81, 0xFF81      # +-qNaN, +-sNaN
+    x[128], x[129], x[130], x[131] = 0x7F80, 0xFF80, three, 0x8000 | five   # +inf, -inf, 3, -5
+    x[256] = 0xFFC0                                              # only a NaN: amax 0
+    x[384], x[385] = 0x7F7F, 0x7FC0                              # bf16 max with a NaN
+    q, s = oracle.quantize_row(x)
+    assert s[0] == np.float32(2.0) / np.float32(448.0)
+    assert q[0] == 0x76 and q[1] == 0x7E                         # 224 = 1.75 * 2^7, 448
+    assert np.all(q[2:6] == 0x7F) and np.all(q[6:128] == 0x00)
+    assert np.isinf(s[1]) and s[1] > 0
+    assert q[128] == 0x7F and q[129] == 0x7F and q[130] == 0x00 and q[131] == 0x80
+    assert np.all(q[132:256] == 0x00)
+    assert s[2] == 0.0 and np.all(q[256:384] == 0x00)            # scale 0: all codes 0
+    assert s[3] == np.float32(3.3895313892515355e38) / np.float32(448.0)
+    assert q[384] == 0x7E and q[385] == 0x7F and np.all(q[386:] == 0x00)
+
+
 def test_fp8_dispatch_rows_hold_token_cast():
     wl = CONFIGS["ll_fp8"].scaled(T=24, H=512)
     x, idx, w = make_workload(wl)
