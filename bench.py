@@ -23,7 +23,10 @@ The headline `value` is
 
     (algorithmic bytes of ep_dispatch + ep_combine) / (t_dispatch + t_combine)
 
-in GB/s, summed over the timed steps.  `roofline` reports the combine kernel
+in GB/s, summed over the timed steps.  Secondary figures: `full_path` adds
+the layout call, and `payload_convention` counts bytes as the pages' own
+benchmark does (one bf16 row per dispatched (token, expert) pair in each
+direction, over the same times).  `roofline` reports the combine kernel
 (one kernel per ep_combine call) against the 8 TB/s HBM3E peak; `traffic`
 comes from committed rocprofv3 FETCH_SIZE / WRITE_SIZE counters when they
 were taken on the current kernel source, else null.  `cpu_baseline` times
@@ -498,6 +501,9 @@ def main():
                          "us_p90": round(float(np.percentile(us, 90)), 2),
                          "alg_bytes": int(B[p]), "GBps": round(gbs, 1),
                          "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    full_us = float(sum(ms[p].mean() for p in ("layout", "dispatch", "combine"))) * 1e3
+    full_b = B["layout"] + B["dispatch"] + B["combine"]
+    payload_b = 2 * 2 * N * H
     c_us = float(ms["combine"].mean()) * 1e3
     achieved = B["combine"] / (c_us * 1e-6) / 1e9
     traffic = load_traffic(B["combine"])
@@ -569,6 +575,16 @@ def main():
                       "note": "ep_dispatch_ll + ep_combine over token_slot, capacity = busiest "
                               "expert's load rounded up to 64 rows (nothing dropped); not part of "
                               "value or ms_per_step"},
+        "full_path": {"us_per_step": round(full_us, 2), "alg_bytes": int(full_b),
+                      "GBps": round(full_b / (full_us * 1e-6) / 1e9, 1),
+                      "pct_of_hbm_peak": round(100 * full_b / (full_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+                      "note": "layout + dispatch + combine, mean event times"},
+        "payload_convention": {"bytes_per_pair": int(payload_b),
+                               "GBps": round(payload_b * args.steps / t_dc / 1e9, 1),
+                               "note": "the pages' benchmark byte count: one bf16 row per dispatched "
+                                       "(token, expert) pair in each direction (2 N H 2 bytes), without "
+                                       "the x read, the output write or the index bytes; same times "
+                                       "as value"},
         "roofline": roofline,
         "roofline_dispatch_copy": roofline_copy,
         "cpu_baseline": cpu,
