@@ -1,0 +1,180 @@
+"""Independent passes of the whole path enqueued on two HIP streams at once.
+
+The library keeps no mutable global state: every counter and partial result
+lives in the caller's workspace, so calls on different streams that touch
+disjoint buffers may overlap.  Each pass below runs every entry point
+(layout, dispatch, combine, FP8 dispatch, cached dispatch, rank-deduplicated
+dispatch and its combine, padded dispatch bf16 / FP8 and its combine); the
+two passes' calls are enqueued alternately, one on each stream, with no
+synchronisation between them.  Every defined output must equal, bit for bit,
+the same pass run alone on the default stream, and the small passes are also
+checked against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_get_dispatch_02_amd import ep
+from combine_get_dispatch_02_amd.workloads import CONFIGS, make_workload
+from test_gpu_parity import dev_bf16, fp8_ulp_ok, host_bits
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def make_pass(name, T=None, H=None, cap=None, seed_extra=0):
+    wl = CONFIGS[name] if T is None else CONFIGS[name].scaled(T=T, H=H)
+    x, idx, w = make_workload(wl, seed_extra=seed_extra)
+    cap = cap or wl.T
+    return dict(wl=wl, x=x, idx=idx, w=w, cap=cap, xd=dev_bf16(x), idxd=torch.from_numpy(idx).to(DEV),
+                wd=torch.from_numpy(w).to(DEV))
+
+
+def calls(p, res):
+    """The pass as a sequence of enqueues; yields after each call so two
+    passes can be interleaved.  Results go into res."""
+    wl, xd, idxd, wd, cap = p["wl"], p["xd"], p["idxd"], p["wd"], p["cap"]
+    E, R, P = wl.E, wl.R, wl.P
+    res["layout"] = ep.ep_get_dispatch_layout(idxd, E, R, P)
+    yield
+    res["d"] = ep.ep_dispatch(xd, idxd, wd, E, R)
+    yield
+    res["c"] = ep.ep_combine(res["d"]["recv_x"], res["d"]["token_row"], wd)
+    yield
+    res["f"] = ep.ep_dispatch_fp8(xd, idxd, wd, E, R)
+    yield
+    res["cached"] = ep.ep_dispatch_cached(xd, res["d"]["token_row"], wl.T * wl.k)
+    yield
+    res["h"] = ep.ep_dispatch_ht(xd, idxd, wd, E, R)
+    yield
+    res["ch"] = ep.ep_combine(res["h"]["recv_x"], res["h"]["token_rank_row"], None)
+    yield
+    res["l"] = ep.ep_dispatch_ll(xd, idxd, wd, E, cap)
+    yield
+    res["cl"] = ep.ep_combine(res["l"]["recv_x"].view(E * cap, wl.H), res["l"]["token_slot"], wd)
+    yield
+    res["l8"] = ep.ep_dispatch_ll_fp8(xd, idxd, wd, E, cap)
+    yield
+
+
+def defined(res, p):
+    """Host copies of every output element the calls define (rows beyond the
+    filled counts are left as they were, so they are not compared)."""
+    wl = p["wl"]
+    E, H = wl.E, wl.H
+    out = {f"layout.{k}": v.cpu().numpy() for k, v in res["layout"].items()}
+    d, f, h, l, l8 = res["d"], res["f"], res["h"], res["l"], res["l8"]
+    n = int(d["recv_expert_offset"][-1].item())
+    out["d.token_row"] = d["token_row"].cpu().numpy()
+    out["d.expert_offset"] = d["recv_expert_offset"].cpu().numpy()
+    out["d.rank_offset"] = d["recv_rank_offset"].cpu().numpy()
+    out["d.src"] = d["recv_src_idx"][:n].cpu().numpy()
+    out["d.w"] = d["recv_topk_weights"][:n].cpu().numpy().view(np.uint32)
+    out["d.x"] = host_bits(d["recv_x"][:n])
+    out["c"] = host_bits(res["c"])
+    out["f.q"] = f["recv_x_fp8"][:n].cpu().numpy()
+    out["f.s"] = f["recv_scales"][:n].cpu().numpy().view(np.uint32)
+    out["f.token_row"] = f["token_row"].cpu().numpy()
+    out["cached"] = host_bits(res["cached"][:n])
+    nh = int(h["recv_rank_offset"][-1].item())
+    out["h.token_rank_row"] = h["token_rank_row"].cpu().numpy()
+    out["h.rank_offset"] = h["recv_rank_offset"].cpu().numpy()
+    out["h.x"] = host_bits(h["recv_x"][:nh])
+    out["h.src"] = h["recv_src_idx"][:nh].cpu().numpy()
+    out["h.topk_idx"] = h["recv_topk_idx"][:nh].cpu().numpy()
+    out["h.w"] = h["recv_topk_weights"][:nh].cpu().numpy().view(np.uint32)
+    out["ch"] = host_bits(res["ch"])
+    cnt = l["recv_count"].cpu().numpy()
+    filled = np.arange(p["cap"])[None, :] < cnt[:, None]
+    fl = torch.from_numpy(filled.reshape(-1)).to(DEV)
+    out["l.count"] = cnt
+    out["l.token_slot"] = l["token_slot"].cpu().numpy()
+    out["l.src"] = l["recv_src_idx"].cpu().numpy()[filled]
+    out["l.w"] = l["recv_topk_weights"].cpu().numpy()[filled].view(np.uint32)
+    out["l.x"] = host_bits(l["recv_x"].view(-1, H)[fl])
+    out["cl"] = host_bits(res["cl"])
+    out["l8.count"] = l8["recv_count"].cpu().numpy()
+    out["l8.q"] = l8["recv_x_fp8"].view(-1, H)[fl].cpu().numpy()
+    out["l8.s"] = l8["recv_scales"].view(E * p["cap"], -1)[fl].cpu().numpy().view(np.uint32)
+    return out
+
+
+def run_alone(p):
+    res = {}
+    for _ in calls(p, res):
+        pass
+    torch.cuda.synchronize()
+    return defined(res, p)
+
+
+def run_interleaved(pa, pb):
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    for s in (sa, sb):
+        s.wait_stream(torch.cuda.current_stream())
+    ra, rb = {}, {}
+    ga, gb = calls(pa, ra), calls(pb, rb)
+    live = [(ga, sa), (gb, sb)]
+    while live:
+        nxt = []
+        for g, s in live:
+            with torch.cuda.stream(s):
+                try:
+                    next(g)
+                    nxt.append((g, s))
+                except StopIteration:
+                    pass
+        live = nxt
+    torch.cuda.synchronize()
+    return defined(ra, pa), defined(rb, pb)
+
+
+def check_same(got, ref, label):
+    assert got.keys() == ref.keys()
+    for key in ref:
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=f"{label}: {key}")
+
+
+def check_oracle(o, p):
+    wl, x, idx, w, cap = p["wl"], p["x"], p["idx"], p["w"], p["cap"]
+    lay = oracle.layout(idx, wl.E, wl.R, wl.P)
+    for key, v in lay.items():
+        np.testing.assert_array_equal(o[f"layout.{key}"], v, err_msg=key)
+    ref = oracle.dispatch(x, idx, w, wl.E, wl.R)
+    n = int(ref["recv_expert_offset"][-1])
+    np.testing.assert_array_equal(o["d.token_row"], ref["token_row"])
+    np.testing.assert_array_equal(o["d.x"], ref["recv_x"][:n])
+    np.testing.assert_array_equal(o["cached"], ref["recv_x"][:n])
+    np.testing.assert_array_equal(o["c"], oracle.combine(ref["recv_x"], ref["token_row"], w))
+    rf = oracle.dispatch_fp8(x, idx, w, wl.E, wl.R)
+    np.testing.assert_array_equal(o["f.s"], rf["recv_scales"][:n].view(np.uint32))
+    assert fp8_ulp_ok(o["f.q"], rf["recv_x_fp8"][:n])
+    rh = oracle.dispatch_ht(x, idx, w, wl.E, wl.R)
+    nh = int(rh["recv_rank_offset"][-1])
+    np.testing.assert_array_equal(o["h.token_rank_row"], rh["token_rank_row"])
+    np.testing.assert_array_equal(o["h.x"], rh["recv_x"][:nh])
+    np.testing.assert_array_equal(o["ch"], oracle.combine(rh["recv_x"], rh["token_rank_row"], None))
+    rl = oracle.dispatch_ll(x, idx, w, wl.E, cap)
+    np.testing.assert_array_equal(o["l.count"], rl["recv_count"])
+    np.testing.assert_array_equal(o["l.token_slot"], rl["token_slot"])
+    np.testing.assert_array_equal(o["l.x"], rl["recv_x"][rl["recv_src_idx"] >= 0])
+    y = rl["recv_x"].reshape(wl.E * cap, wl.H)
+    np.testing.assert_array_equal(o["cl"], oracle.combine(y, rl["token_slot"], w))
+
+
+@pytest.mark.parametrize("pair", ["small", "full"])
+def test_two_streams_interleaved(pair):
+    if pair == "small":
+        pa = make_pass("dsv3", T=300, H=1024, cap=12, seed_extra=11)
+        pb = make_pass("skewed", T=700, H=512, cap=40, seed_extra=12)
+    else:
+        pa = make_pass("dsv3", cap=192)
+        pb = make_pass("skewed", cap=7488)
+    print(f"[streams {pair}] {pa['wl'].describe()} | {pb['wl'].describe()}", flush=True)
+    alone_a, alone_b = run_alone(pa), run_alone(pb)
+    got_a, got_b = run_interleaved(pa, pb)
+    check_same(got_a, alone_a, "stream a")
+    check_same(got_b, alone_b, "stream b")
+    if pair == "small":
+        check_oracle(got_a, pa)
+        check_oracle(got_b, pb)
