@@ -75,6 +75,7 @@ def _fp8_pins():
         tf.test_quantize_row_bounds(s, seed)
     tf.test_zero_and_signed_zero_blocks()
     tf.test_tiny_amax_keeps_denormal_scale()
+    tf.test_non_finite_blocks()
     tf.test_fp8_dispatch_rows_hold_token_cast()
 
 
@@ -120,6 +121,9 @@ MUTATIONS = {
     "e4m3_sign_dropped": ("uint8_t sign = signbit(v) ? 0x80 : 0x00;", "uint8_t sign = 0x00;", _fp8_pins),
     "amax_signed": ("float v = fabsf(bf16_to_f32(xrow[h]));", "float v = bf16_to_f32(xrow[h]);", _fp8_pins),
     "scale_447": ("float s = a / 448.0f;", "float s = a / 447.0f;", _fp8_pins),
+    "amax_nan_poisons": ("if (v > a) a = v;", "if (!(v <= a)) a = v;", _fp8_pins),
+    "e4m3_nan_keeps_sign": ("if (isnan(v)) return 0x7F;", "if (isnan(v)) return signbit(v) ? 0xFF : 0x7F;",
+                            _fp8_pins),
     "scale_reciprocal_multiply": ("oracle_e4m3_encode(bf16_to_f32(xrow[h]) / s)",
                                   "oracle_e4m3_encode(bf16_to_f32(xrow[h]) * s)", _fp8_pins),
     # combine and bf16 rounding
