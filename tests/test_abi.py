@@ -5,6 +5,7 @@ anything (every call below fails validation, so no HIP call is reached)."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -233,3 +234,28 @@ def test_misaligned_workspace_rejected():
     assert _ht(ws=odd) == EINVAL
     assert _ll(ws=odd) == EINVAL
     assert b"4-byte aligned" in ep.lib().ep_last_error()
+
+
+@pytest.mark.parametrize("compiler,std", [("gcc", "-std=c99"), ("g++", "-std=c++17")])
+def test_header_compiles_as_c_and_cpp(compiler, std, tmp_path):
+    """include/ep.h is a plain C header (usable from C and C++) that names no
+    HIP or torch type."""
+    src = tmp_path / ("use_ep.c" if compiler == "gcc" else "use_ep.cpp")
+    src.write_text('#include "ep.h"\nint ep_header_probe(void) { return EP_OK + EP_MAX_TOPK; }\n')
+    subprocess.check_call([compiler, std, "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only",
+                           "-I", os.path.join(ROOT, "include"), str(src)])
+    text = open(HEADER).read()
+    assert "hip" not in re.sub(r"/\*.*?\*/", "", text, flags=re.S).replace("hipStream_t", "")
+
+
+def test_c_caller_compiles_and_links(tmp_path):
+    """The plain-C caller of the GPU tests compiles (C99, -Werror) and links
+    against libep.so and the HIP runtime."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "build_caller", os.path.join(ROOT, "tests", "c_caller", "build_caller.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    ep.lib()                                   # libep.so is built
+    mod.EXE = str(tmp_path / "ep_c_caller")
+    assert os.path.exists(mod.build())
