@@ -65,12 +65,12 @@ extern "C" {
 typedef enum {
     EP_OK = 0,
     EP_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, misalignment, ... */
-    EP_ERR_UNSUPPORTED = 2,        /* valid but beyond this build's limits      */
+    EP_ERR_UNSUPPORTED = 2,        /* valid but beyond the library's limits     */
     EP_ERR_WORKSPACE_TOO_SMALL = 3,
     EP_ERR_HIP = 4                 /* a HIP runtime call or launch failed        */
 } ep_status_t;
 
-/* Limits of this build (EP_ERR_UNSUPPORTED beyond them). */
+/* Limits of the library (EP_ERR_UNSUPPORTED beyond them). */
 #define EP_MAX_TOPK 64          /* num_topk                                   */
 #define EP_MAX_RANKS 64         /* num_ranks                                  */
 #define EP_MAX_EXPERTS 2048     /* num_experts                                */
