@@ -9,8 +9,9 @@ reported beside the headline and not part of it: the rank-deduplicated pair
 ep_dispatch_ht -> ep_combine (unweighted, over the per-rank rows), the padded
 expert-major (low-latency) layout ep_dispatch_ll -> ep_combine (over the slot
 map) -> ep_dispatch_ll_fp8 with the capacity set to the busiest expert's load
-rounded up to 64 rows (nothing dropped), and ep_dispatch_cached (the copy
-kernel alone, reusing token_row).  Before each
+rounded up to 64 rows (nothing dropped), ep_dispatch_cached (the copy
+kernel alone, reusing token_row) and ep_dispatch_fp8_cached (the FP8 cast and
+copy alone).  Before each
 phase (outside its events) a 512 MiB write followed by a 512 MiB read of
 another buffer evicts L2 and the 256 MB Infinity Cache: the phase's inputs
 are then only in HBM and the caches hold clean, unrelated lines, so no
@@ -93,6 +94,8 @@ def algorithmic_bytes(wl, n_ht=None, n_ll=None):
         combine=4 * T * k + 4 * T * k + 2 * N * H + 2 * T * H,
         # the copy alone, driven by a saved token_row (x read, rows written, map read)
         dispatch_cached=2 * T * H + 2 * N * H + 4 * T * k,
+        # the FP8 cast-and-copy alone (x read, codes and scales written, map read)
+        dispatch_fp8_cached=2 * T * H + N * H + 4 * N * (H // 128) + 4 * T * k,
         dispatch_ht=8 * T * k + 4 * T * k + 2 * T * H + 2 * n * H + ht_maps,
         combine_ht=4 * T * R + 2 * n * H + 2 * T * H,
         # padded layout, m slots kept: token_slot, src and weight per kept
@@ -380,11 +383,13 @@ def main():
     ws_ll = torch.empty(ep.ep_dispatch_ll_workspace_bytes(T, k, E), dtype=torch.uint8, device=dev)
     comb_ll = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     cached = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    cached8 = dict(recv_x_fp8=torch.empty((N, H), dtype=torch.uint8, device=dev),
+                   recv_scales=torch.empty((N, H // 128), dtype=torch.float32, device=dev))
     flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     flush_src = torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
 
     phases = ["layout", "dispatch", "combine", "dispatch_fp8", "dispatch_ht", "combine_ht",
-              "dispatch_ll", "combine_ll", "dispatch_ll_fp8", "dispatch_cached"]
+              "dispatch_ll", "combine_ll", "dispatch_ll_fp8", "dispatch_cached", "dispatch_fp8_cached"]
 
     def flush(i):
         if not args.no_flush:
@@ -430,9 +435,13 @@ def main():
         ev[17].record()
         ep.ep_dispatch_cached(xd, disp["token_row"], N, out=cached)
         ev[18].record()
+        flush(i + 9)
+        ev[19].record()
+        ep.ep_dispatch_fp8_cached(xd, fp8["token_row"], N, out=cached8)
+        ev[20].record()
 
     def events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(19)]
+        return [torch.cuda.Event(enable_timing=True) for _ in range(21)]
 
     if args.graph:
         graph_mode(args, wl, ep, torch, np, idxd, xd, wd, lay, ws_l, disp, ws_d, comb, fp8)
@@ -483,7 +492,7 @@ def main():
 
     ms = {p: np.array([e[a].elapsed_time(e[b]) for e in evs])
           for p, (a, b) in zip(phases, [(0, 1), (1, 2), (3, 4), (5, 6), (7, 8), (9, 10), (11, 12),
-                                        (13, 14), (15, 16), (17, 18)])}
+                                        (13, 14), (15, 16), (17, 18), (19, 20)])}
     B = algorithmic_bytes(wl, n_ht, n_ll)
     t_dc = float(ms["dispatch"].sum() + ms["combine"].sum()) / 1e3
     value = (B["dispatch"] + B["combine"]) * args.steps / t_dc / 1e9
@@ -524,6 +533,12 @@ def main():
                                "x read from HBM)", "bound": "hbm", "achieved": round(k_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
                      "alg_bytes_per_launch": int(B["dispatch_cached"]), "avg_launch_us": round(k_us, 2)}
+    q_us = float(ms["dispatch_fp8_cached"].mean()) * 1e3
+    q_gbs = B["dispatch_fp8_cached"] / (q_us * 1e-6) / 1e9
+    roofline_fp8 = {"kernel": "copy_fp8_kernel (ep_dispatch_fp8_cached: the FP8 cast and copy alone, "
+                              "x read from HBM)", "bound": "hbm", "achieved": round(q_gbs, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(q_gbs / HBM_PEAK_GBS, 4),
+                    "alg_bytes_per_launch": int(B["dispatch_fp8_cached"]), "avg_launch_us": round(q_us, 2)}
     roofline = {"kernel": "combine_kernel<2, 8, true> (ep_combine)", "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -587,6 +602,7 @@ def main():
                                        "as value"},
         "roofline": roofline,
         "roofline_dispatch_copy": roofline_copy,
+        "roofline_fp8_copy": roofline_fp8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
