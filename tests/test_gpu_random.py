@@ -8,7 +8,8 @@ padded layout (bf16 and FP8) and the combines over each map: maps and bytes
 bit-exact, FP8 codes within one step (scales bit-exact), combines bit-exact.
 The shapes cross the kernels' internal limits: the one-launch small batch
 (T*k <= 2048), the one-launch receive order (<= 2^15 slots) and beyond, the
-one-launch rank-deduplicated index (R, k <= 16) and beyond.
+one-launch rank-deduplicated index (R, k <= 16) and beyond.  A second,
+wider draw reaches top-64, 2048 experts, 64 ranks and 40000 tokens.
 """
 import numpy as np
 import pytest
@@ -46,10 +47,47 @@ def draw(seed):
     return T, k, E, R, P, H, idx, x, w, cap
 
 
+def draw_wide(seed):
+    """Wider shapes: top-k to 64, up to 2048 experts and 64 ranks, up to
+    40000 tokens (H = 128 once T*k passes 4000, T*k at most 300000), half of
+    the slots empty or out of range in some cases."""
+    rng = np.random.default_rng([11, seed])
+    R = int(rng.choice([1, 2, 5, 8, 16, 32, 33, 64]))
+    epr = int(rng.choice([1, 2, 4, 8, 32]))
+    E = min(R * epr, 2048 // R * R)
+    k = int(rng.integers(1, min(E, 64) + 1)) if rng.random() < 0.7 else int(rng.integers(1, 65))
+    T = int(rng.choice([1, 2, 31, 64, 65, 257, 2049, 4097, 9000, 16385, 40000]))
+    H = 128 * int(rng.choice([1, 2, 7, 56]))
+    if T * k > 4000:
+        H = 128
+    if T * k > 300000:
+        T = max(1, 300000 // k)
+    P = int(rng.choice([d for d in range(1, R + 1) if R % d == 0]))
+    if rng.random() < 0.5 and k <= E:
+        idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int64)
+    else:
+        idx = rng.integers(0, E, size=(T, k)).astype(np.int64)
+    bad = rng.random((T, k)) < rng.choice([0.0, 0.02, 0.5])
+    idx[bad] = rng.choice([-1, E, E + 1000, -3], size=int(bad.sum()))
+    x = (rng.standard_normal((T, H)).astype(np.float32) * rng.choice([1.0, 4.0]))
+    x = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    w = rng.random((T, k)).astype(np.float32) if rng.random() < 0.8 else None
+    cap = int(rng.choice([1, 3, max(1, T * k // max(E, 1)), T]))
+    return T, k, E, R, P, H, idx, x, w, cap
+
+
 @pytest.mark.parametrize("seed", range(60))
 def test_random_shapes_every_entry_point(seed):
-    T, k, E, R, P, H, idx, x, w, cap = draw(seed)
-    print(f"[random {seed}] T={T} k={k} E={E} R={R} P={P} H={H} cap={cap} w={w is not None}", flush=True)
+    run_every_entry_point(f"random {seed}", *draw(seed))
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_wide_random_shapes_every_entry_point(seed):
+    run_every_entry_point(f"wide {seed}", *draw_wide(seed))
+
+
+def run_every_entry_point(label, T, k, E, R, P, H, idx, x, w, cap):
+    print(f"[{label}] T={T} k={k} E={E} R={R} P={P} H={H} cap={cap} w={w is not None}", flush=True)
     xd, idxd = dev_bf16(x), torch.from_numpy(idx).to(DEV)
     wd = None if w is None else torch.from_numpy(w).to(DEV)
 
