@@ -36,10 +36,14 @@ constexpr int kHistBatch = 64;
 constexpr int kSlotsPerLane = kMaxTileSlots / kIndexThreads;
 // Fused receive-order kernel: every block histograms all T*k slots itself.
 constexpr int kFusedThreads = 1024;
-// Slots per thread per sweep step (loads in flight).  8 measured ~1 us faster
-// per ep_dispatch than 32 at 4096 x 8 slots, despite four round trips instead
-// of one: the smaller unrolled batch costs less.
+// Loads per thread per sweep step.  8 measured ~1 us faster per ep_dispatch
+// than 32 at 4096 x 8 slots, despite more round trips: the smaller unrolled
+// batch costs less.  With 16-byte loads (two ids each, when topk_idx is
+// 16-byte aligned) the same 8 loads cover 16 slots, and the kernel is 1.6 us
+// shorter at 4096 x 8 slots than with 8-byte loads (14.5 vs 16.1 us by
+// kernel trace, x prefetch included); 4 or 16 pair loads were slower.
 constexpr int kFusedBatch = 8;
+typedef long long i64x2 __attribute__((ext_vector_type(2)));
 
 // Per-tile expert histogram: hist[tile][e] = valid slots of the tile's tokens
 // routed to e (LDS atomics; integer sums do not depend on order).
@@ -274,6 +278,19 @@ __global__ __launch_bounds__(kIndexThreads) void rows_kernel(
 // that follows then finds that part of x in the 256 MB Infinity Cache
 // instead of HBM (x is still read from HBM exactly once).
 constexpr int kFusedWeights = kMaxTileSlots / kFusedThreads;
+
+// One id of the sweep: counted in LDS as before or inside the tile (pre /
+// rest), and kept in LDS when it belongs to the tile.
+__device__ __forceinline__ void sweep_count(int64_t v, unsigned sl, unsigned lo, unsigned hi, int E,
+                                            int32_t* pre, int32_t* rest, int32_t* tile_ids) {
+    const bool valid = v >= 0 && v < E;
+    if (valid) atomicAdd(sl < lo ? &pre[v] : &rest[v], 1);
+    if (sl >= lo && sl < hi) tile_ids[sl - lo] = valid ? static_cast<int32_t>(v) : -1;
+}
+
+// kPairs: topk_idx is 16-byte aligned and each load brings two consecutive
+// ids (slots 2p, 2p+1).
+template <bool kPairs>
 __global__ __launch_bounds__(kFusedThreads) void rows_fused_kernel(
     const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int64_t T,
     int k, int E, int R, int tile_tokens, int nbits, int32_t* __restrict__ token_row,
@@ -317,22 +334,40 @@ __global__ __launch_bounds__(kFusedThreads) void rows_fused_kernel(
     const unsigned total_slots = static_cast<unsigned>(T * k);
     const unsigned lo = static_cast<unsigned>(s0);
     const unsigned hi = lo + static_cast<unsigned>(S);
-    for (unsigned b0 = 0; b0 < total_slots; b0 += kFusedThreads * kFusedBatch) {
-        int64_t v[kFusedBatch];
+    // Addresses are a scalar base plus a 32-bit byte offset (one VGPR of
+    // address per load).
+    const char* ids_base = reinterpret_cast<const char*>(topk_idx);
+    if (kPairs) {
+        for (unsigned b0 = 0; b0 < total_slots; b0 += 2 * kFusedThreads * kFusedBatch) {
+            i64x2 v[kFusedBatch];
 #pragma unroll
-        for (int i = 0; i < kFusedBatch; ++i) {
-            const unsigned sl = b0 + i * kFusedThreads + threadIdx.x;
-            // scalar base + 32-bit byte offset: one VGPR of address per load
-            v[i] = sl < total_slots
-                       ? *reinterpret_cast<const int64_t*>(reinterpret_cast<const char*>(topk_idx) + sl * 8u)
-                       : -1;
+            for (int i = 0; i < kFusedBatch; ++i) {
+                const unsigned sl = b0 + 2 * (i * kFusedThreads + threadIdx.x);
+                if (sl + 1 < total_slots) {
+                    v[i] = *reinterpret_cast<const i64x2*>(ids_base + sl * 8u);
+                } else {
+                    v[i][0] = sl < total_slots ? *reinterpret_cast<const int64_t*>(ids_base + sl * 8u) : -1;
+                    v[i][1] = -1;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kFusedBatch; ++i) {
+                const unsigned sl = b0 + 2 * (i * kFusedThreads + threadIdx.x);
+                sweep_count(v[i][0], sl, lo, hi, E, pre, rest, tile_ids);
+                sweep_count(v[i][1], sl + 1, lo, hi, E, pre, rest, tile_ids);
+            }
         }
+    } else {
+        for (unsigned b0 = 0; b0 < total_slots; b0 += kFusedThreads * kFusedBatch) {
+            int64_t v[kFusedBatch];
 #pragma unroll
-        for (int i = 0; i < kFusedBatch; ++i) {
-            const unsigned sl = b0 + i * kFusedThreads + threadIdx.x;
-            const bool valid = v[i] >= 0 && v[i] < E;
-            if (valid) atomicAdd(sl < lo ? &pre[v[i]] : &rest[v[i]], 1);
-            if (sl >= lo && sl < hi) tile_ids[sl - lo] = valid ? static_cast<int32_t>(v[i]) : -1;
+            for (int i = 0; i < kFusedBatch; ++i) {
+                const unsigned sl = b0 + i * kFusedThreads + threadIdx.x;
+                v[i] = sl < total_slots ? *reinterpret_cast<const int64_t*>(ids_base + sl * 8u) : -1;
+            }
+#pragma unroll
+            for (int i = 0; i < kFusedBatch; ++i)
+                sweep_count(v[i], b0 + i * kFusedThreads + threadIdx.x, lo, hi, E, pre, rest, tile_ids);
         }
     }
 #pragma unroll
@@ -726,7 +761,9 @@ hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weig
         const size_t lds = fused_lds;
         // Prefetch blocks only while that part of x fits the cache comfortably.
         const int pf_blocks = pf_bytes > 0 ? prefetch_blocks(pf_bytes) : 0;
-        hipLaunchKernelGGL(rows_fused_kernel, dim3(ntiles + pf_blocks), dim3(kFusedThreads), lds, stream,
+        const bool pairs = (reinterpret_cast<uintptr_t>(topk_idx) & 15u) == 0;
+        hipLaunchKernelGGL(pairs ? rows_fused_kernel<true> : rows_fused_kernel<false>,
+                           dim3(ntiles + pf_blocks), dim3(kFusedThreads), lds, stream,
                            topk_idx, w_in, T, k, E, R, tt, nbits, token_row, recv_src_idx, w_out,
                            expert_offset, rank_offset, ntiles, cap, recv_count,
                            static_cast<const u32x4*>(x), pf_bytes / 16, pf_sink);

@@ -420,19 +420,23 @@ def test_edge_non_finite_tokens(T, k):
         np.testing.assert_array_equal(got[~nan_exp], exp[~nan_exp])
 
 
-@pytest.mark.parametrize("T,k,E,R,H,mask", [
-    (40000, 8, 256, 8, 64, 0.0),      # T*k > 2^15: histogram launch + ranking launch
-    (33000, 8, 64, 8, 64, 0.05),      # same path, masked slots, ragged last tile
-    (3000, 6, 2048, 64, 128, 0.02),   # many experts and ranks (fused path, large LDS)
-    (20000, 16, 2048, 64, 16, 0.0),   # many experts, two launches, k > 8
-    (4096, 8, 256, 8, 64, 0.03),      # T*k = 2^15: the last fused size
-    (4097, 8, 256, 8, 64, 0.03),      # one token more: two launches
+@pytest.mark.parametrize("T,k,E,R,H,mask,ids_off", [
+    (40000, 8, 256, 8, 64, 0.0, 0),      # T*k > 2^15: histogram launch + ranking launch
+    (33000, 8, 64, 8, 64, 0.05, 0),      # same path, masked slots, ragged last tile
+    (3000, 6, 2048, 64, 128, 0.02, 0),   # many experts and ranks (fused path, large LDS)
+    (20000, 16, 2048, 64, 16, 0.0, 0),   # many experts, two launches, k > 8
+    (4096, 8, 256, 8, 64, 0.03, 0),      # T*k = 2^15: the last fused size
+    (4096, 8, 256, 8, 64, 0.03, 1),      # same, ids only 8-byte aligned (one id per load)
+    (3001, 7, 256, 8, 64, 0.02, 0),      # odd T*k: the last id pair holds one id
+    (3001, 7, 256, 8, 64, 0.02, 1),      # odd T*k, ids only 8-byte aligned
+    (4097, 8, 256, 8, 64, 0.03, 0),      # one token more: two launches
 ])
-def test_parity_receive_order_paths(T, k, E, R, H, mask):
+def test_parity_receive_order_paths(T, k, E, R, H, mask, ids_off):
     """Both receive-order paths (one fused launch up to 2^15 slots, two
     launches above; both carry the x prefetch) against the oracle, element by
-    element."""
-    _say(f"[parity-paths] T={T} k={k} E={E} R={R} H={H} mask={mask}")
+    element.  ids_off = 1 places topk_idx one int64 into a device buffer, so
+    the fused sweep cannot read ids in 16-byte pairs."""
+    _say(f"[parity-paths] T={T} k={k} E={E} R={R} H={H} mask={mask} ids_off={ids_off}")
     rng = np.random.default_rng(T + E)
     idx = np.argsort(rng.random((T, E), dtype=np.float32), axis=1)[:, :k].astype(np.int64)
     if mask:
@@ -444,7 +448,11 @@ def test_parity_receive_order_paths(T, k, E, R, H, mask):
     ref_l = oracle.layout(idx, E, R, P)
     ref_d = oracle.dispatch(x, idx, w, E, R)
     N = int(ref_d["recv_expert_offset"][-1])
-    xd, idxd, wd = dev_bf16(x), torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV)
+    xd, wd = dev_bf16(x), torch.from_numpy(w).to(DEV)
+    idx_buf = torch.empty(T * k + ids_off, dtype=torch.int64, device=DEV)
+    idxd = idx_buf[ids_off:].view(T, k)
+    idxd.copy_(torch.from_numpy(idx))
+    assert (idxd.data_ptr() % 16 == 0) == (ids_off == 0)
     check_layout(gpu_layout(idxd, wl), ref_l)
     out = prefilled_dispatch_out(T, k, H, E, R, fp8=False)
     d = ep.ep_dispatch(xd, idxd, wd, E, R, out=out)
