@@ -7,9 +7,11 @@
 // Two launches, no atomics on global memory and no zero-fill (one when the
 // batch fits a single block of 256 tokens):
 //   1. layout_partial: one token per thread, 256 tokens per block.  Each block
-//      builds its expert / rank / group histograms in LDS, writes the
-//      is_token_in_rank rows of its tokens, and stores its histograms in the
-//      workspace.
+//      builds its expert / rank / group histograms in LDS (experts by LDS
+//      atomics; ranks and groups by one wave64 ballot per rank or group, whose
+//      popcount lane r of the wave accumulates, then one LDS add per lane),
+//      writes the is_token_in_rank rows of its tokens, and stores its
+//      histograms in the workspace.
 //   2. layout_reduce: one thread per output counter sums the per-block
 //      histograms (integer sums: the result does not depend on order).
 #include "ep_device.h"
@@ -54,12 +56,21 @@ __global__ __launch_bounds__(kLayoutTokensPerBlock) void layout_partial_kernel(
     }
     masks[threadIdx.x] = m;
     uint64_t gm = 0;
-    for (uint64_t b = m; b; b &= b - 1) {
-        const int r = __builtin_ctzll(b);
-        atomicAdd(&h_r[r], 1);
-        gm |= uint64_t(1) << (r / P);
+    for (uint64_t b = m; b; b &= b - 1) gm |= uint64_t(1) << (__builtin_ctzll(b) / P);
+    // Tokens of this wave reaching rank r (group g): popcount of one ballot,
+    // kept by lane r (g).  R, G <= 64.
+    const int lane = lane_id();
+    int my_r = 0, my_g = 0;
+    for (int r = 0; r < R; ++r) {
+        const int c = __popcll(ballot((m >> r) & 1u));
+        if (lane == r) my_r = c;
     }
-    for (uint64_t b = gm; b; b &= b - 1) atomicAdd(&h_g[__builtin_ctzll(b)], 1);
+    for (int g = 0; g < G; ++g) {
+        const int c = __popcll(ballot((gm >> g) & 1u));
+        if (lane == g) my_g = c;
+    }
+    if (lane < R && my_r) atomicAdd(&h_r[lane], my_r);
+    if (lane < G && my_g) atomicAdd(&h_g[lane], my_g);
     __syncthreads();
 
     // is_token_in_rank rows of this block are nt * R consecutive bytes.
