@@ -39,13 +39,18 @@ def prefilled(T, k, H, R, weights):
                 token_rank_row=torch.full((max(T, 1) if T else 0, R), -9, dtype=torch.int32, device=DEV))
 
 
-def run_case(x, idx, w, E, R, combine_y=None):
+def run_case(x, idx, w, E, R, combine_y=None, ids_off=0):
+    """ids_off = 1 places topk_idx one int64 into a device buffer (8-byte
+    aligned only), so the one-launch index kernel reads one id per load."""
     T, k = idx.shape
     H = x.shape[1]
     ref = oracle.dispatch_ht(x, idx, w, E, R)
     n = int(ref["recv_rank_offset"][-1])
     out = prefilled(T, k, H, R, w is not None)
-    d = ep.ep_dispatch_ht(dev_bf16(x), torch.from_numpy(idx).to(DEV),
+    idx_buf = torch.empty(T * k + ids_off, dtype=torch.int64, device=DEV)
+    idxd = idx_buf[ids_off:].view(T, k)
+    idxd.copy_(torch.from_numpy(idx))
+    d = ep.ep_dispatch_ht(dev_bf16(x), idxd,
                           None if w is None else torch.from_numpy(w).to(DEV), E, R, out=out)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(d["recv_rank_offset"].cpu().numpy(), ref["recv_rank_offset"])
@@ -132,6 +137,19 @@ def test_ht_edge_shapes(T, k, E, R, H):
     w = rng.random((T, k)).astype(np.float32)
     run_case(x, idx, w, E, R)
     run_case(x, idx, None, E, R)
+
+
+@pytest.mark.parametrize("T,k,ids_off", [(300, 8, 0), (300, 8, 1), (129, 16, 1), (129, 6, 0)])
+def test_ht_id_alignment(T, k, ids_off):
+    """The one-launch index kernel reads a token's ids in 16-byte pairs when k
+    is even and topk_idx 16-byte aligned, one by one otherwise."""
+    rng = np.random.default_rng(T + k + ids_off)
+    E, R, H = 64, 8, 64
+    idx = np.argsort(rng.random((T, E), dtype=np.float32), axis=1)[:, :k].astype(np.int64)
+    idx[rng.random((T, k)) < 0.05] = -1
+    x = rng.integers(0, 0x7F00, size=(T, H)).astype(np.uint16)
+    w = rng.random((T, k)).astype(np.float32)
+    run_case(x, idx, w, E, R, ids_off=ids_off)
 
 
 def test_ht_empty_batch_and_all_empty_slots():
