@@ -139,7 +139,8 @@ def test_ht_edge_shapes(T, k, E, R, H):
     run_case(x, idx, None, E, R)
 
 
-@pytest.mark.parametrize("T,k,ids_off", [(300, 8, 0), (300, 8, 1), (129, 16, 1), (129, 6, 0)])
+@pytest.mark.parametrize("T,k,ids_off", [(300, 8, 0), (300, 8, 1), (129, 16, 0), (129, 16, 1),
+                                         (129, 6, 0), (1001, 2, 0), (77, 4, 0), (77, 4, 1)])
 def test_ht_id_alignment(T, k, ids_off):
     """The one-launch index kernel reads a token's ids in 16-byte pairs when k
     is even and topk_idx 16-byte aligned, one by one otherwise."""
