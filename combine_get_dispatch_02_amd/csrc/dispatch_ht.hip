@@ -28,9 +28,11 @@
 //                 among the tile's tokens routed to the same rank from one
 //                 ballot per rank per wave; writes token_rank_row
 //   ht_meta       each row's source token and remapped top-k ids and weights,
-//                 one thread per (token, rank, slot): coalesced stores from
-//                 T * R * k threads rather than per-lane scattered ones from
-//                 the few blocks of ht_rows
+//                 one thread per (token, slot): from the token's rank mask,
+//                 the thread writes its slot's entry of every row the token
+//                 has, so the k threads of a token store each row's k entries
+//                 together (coalesced), with no thread per unused (token,
+//                 rank) pair
 //   copy          the bf16 copy kernel of ep_dispatch, driven by the [T, R]
 //                 map token_rank_row instead of the [T, k] token_row
 #include "../../include/ep.h"
@@ -155,21 +157,32 @@ __global__ __launch_bounds__(256) void ht_meta_kernel(
     int64_t* __restrict__ recv_topk_idx, float* __restrict__ recv_w, int64_t T, int k, int E,
     int R) {
     const int epr = E / R;
-    const int64_t n = T * R * k;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
-        const int64_t tr = i / k;            // t * R + r
-        const int j = static_cast<int>(i - tr * k);
-        const int row = token_rank_row[tr];
-        if (row < 0) continue;
-        const int64_t t = tr / R;
-        const int r = static_cast<int>(tr - t * R);
-        const int64_t e = topk_idx[t * k + j];
-        const bool local = e >= 0 && e < E && rank_of(e, epr) == r;
-        recv_topk_idx[static_cast<int64_t>(row) * k + j] = local ? e - static_cast<int64_t>(r) * epr : -1;
-        if (recv_w)
-            recv_w[static_cast<int64_t>(row) * k + j] = (local && topk_weights) ? topk_weights[t * k + j] : 0.0f;
-        if (j == 0) recv_src_idx[row] = static_cast<int32_t>(t);
+    // T * k < 2^31 (checked by the API), so slot indices and their division by
+    // k stay in 32 bits (a 64-bit division is a long software sequence here).
+    const uint32_t n = static_cast<uint32_t>(T * k);
+    const uint32_t uk = static_cast<uint32_t>(k);
+    const uint32_t stride = gridDim.x * blockDim.x;
+    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const uint32_t t = i / uk;
+        const int j = static_cast<int>(i - t * uk);
+        const int64_t* ids = topk_idx + static_cast<int64_t>(t) * k;
+        uint64_t m = 0;                       // ranks the token reaches (R <= 64)
+        for (int jj = 0; jj < k; ++jj) {
+            const int64_t e = ids[jj];
+            if (e >= 0 && e < E) m |= uint64_t(1) << rank_of(e, epr);
+        }
+        const int64_t e = ids[j];
+        const int rj = (e >= 0 && e < E) ? rank_of(e, epr) : -1;
+        const float wj = (recv_w && topk_weights && rj >= 0) ? topk_weights[i] : 0.0f;
+        for (; m; m &= m - 1) {
+            const int r = __builtin_ctzll(m);
+            const int row = token_rank_row[static_cast<int64_t>(t) * R + r];
+            if (row < 0) continue;
+            const bool local = r == rj;
+            recv_topk_idx[static_cast<int64_t>(row) * k + j] = local ? e - static_cast<int64_t>(r) * epr : -1;
+            if (recv_w) recv_w[static_cast<int64_t>(row) * k + j] = local ? wj : 0.0f;
+            if (j == 0) recv_src_idx[row] = static_cast<int32_t>(t);
+        }
     }
 }
 
@@ -362,7 +375,7 @@ hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const floa
                        E, R, hist);
     hipLaunchKernelGGL(ht_rows_kernel, dim3(ntiles), dim3(kHtTile), 0, stream, topk_idx, T, k, E,
                        R, ntiles, hist, token_rank_row, rank_offset);
-    const int64_t n = T * R * k;
+    const int64_t n = T * k;                          // one thread per (token, slot)
     const int64_t blocks = ceil_div(n, 256);
     const int64_t cap = kMaxLaunchThreads / 256;
     hipLaunchKernelGGL(ht_meta_kernel, dim3(static_cast<unsigned>(blocks < cap ? blocks : cap)),
