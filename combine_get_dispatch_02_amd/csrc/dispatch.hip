@@ -541,6 +541,7 @@ __global__ __launch_bounds__(256) void copy_fp8_kernel(const u32x4* __restrict__
 // from position cap on, and block 0 writes recv_count[e] = min(count, cap).
 // LDS: cnt_pre[E], cnt_all[E], wave_tot[16], own[EP_MAX_TOPK], rows[EP_MAX_TOPK].
 constexpr int kSmallMaxK = 64;
+constexpr int kSmallBatch = 4;     // id loads per thread per step of the small-batch sweep
 
 __device__ int block_exclusive_scan_rt(int32_t* a, int n, int32_t* wave_tot) {
     const int nthreads = blockDim.x;
@@ -591,24 +592,46 @@ __device__ void small_token_rows(const int64_t* __restrict__ topk_idx,
     int32_t* wave_tot = lds + 2 * E;
     int32_t* own = wave_tot + 16;
     const int j = threadIdx.x;
-    // The token's weights (needed only by its first block): requested first.
+    // The token's weights (needed only by its first block) and the first
+    // batch of ids are requested before anything waits, so they share one
+    // round trip with the caller's x loads: kSmallBatch loads per thread,
+    // indices clamped to the last slot (no branch around a load, which would
+    // make the compiler wait for it).
     const float wj = (write_maps && recv_w && j < k) ? topk_weights[t * k + j] : 0.0f;
+    const int total_slots = static_cast<int>(T * k);
+    const int first = static_cast<int>(t * k);
+    const int step = kSmallBatch * static_cast<int>(blockDim.x);
+    int64_t v[kSmallBatch];
+#pragma unroll
+    for (int u = 0; u < kSmallBatch; ++u) {
+        const int sl = u * static_cast<int>(blockDim.x) + static_cast<int>(threadIdx.x);
+        v[u] = topk_idx[sl < total_slots ? sl : total_slots - 1];
+    }
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         cnt_pre[e] = 0;
         cnt_all[e] = 0;
     }
     __syncthreads();
-    const int total_slots = static_cast<int>(T * k);
-    const int first = static_cast<int>(t * k);
-#pragma unroll 4
-    for (int sl = threadIdx.x; sl < total_slots; sl += blockDim.x) {
-        const int64_t e = topk_idx[sl];
-        const bool valid = e >= 0 && e < E;
-        if (valid) {
-            atomicAdd(&cnt_all[e], 1);
-            if (sl < first) atomicAdd(&cnt_pre[e], 1);
+    for (int s0 = 0; s0 < total_slots; s0 += step) {
+        if (s0 > 0) {
+#pragma unroll
+            for (int u = 0; u < kSmallBatch; ++u) {
+                const int sl = s0 + u * static_cast<int>(blockDim.x) + static_cast<int>(threadIdx.x);
+                v[u] = topk_idx[sl < total_slots ? sl : total_slots - 1];
+            }
         }
-        if (sl >= first && sl < first + k) own[sl - first] = valid ? static_cast<int32_t>(e) : -1;
+#pragma unroll
+        for (int u = 0; u < kSmallBatch; ++u) {
+            const int sl = s0 + u * static_cast<int>(blockDim.x) + static_cast<int>(threadIdx.x);
+            if (sl >= total_slots) continue;
+            const int64_t e = v[u];
+            const bool valid = e >= 0 && e < E;
+            if (valid) {
+                atomicAdd(&cnt_all[e], 1);
+                if (sl < first) atomicAdd(&cnt_pre[e], 1);
+            }
+            if (sl >= first && sl < first + k) own[sl - first] = valid ? static_cast<int32_t>(e) : -1;
+        }
     }
     __syncthreads();
     if (cap > 0) {
@@ -655,11 +678,13 @@ __global__ __launch_bounds__(512) void dispatch_small_bf16_kernel(
     const int64_t t = blockIdx.x / segs;
     const int seg = static_cast<int>(blockIdx.x - t * segs);
     const int v0 = seg * (kCopyVec * kWave) + lane;
+    // Both x loads issued before either is waited on: the vector index is
+    // clamped to the row (lanes past its end store nothing).
     u32x4 val[kCopyVec];
 #pragma unroll
     for (int u = 0; u < kCopyVec; ++u) {
         const int v = v0 + u * kWave;
-        if (v < V) val[u] = x[t * V + v];
+        val[u] = x[t * V + (v < V ? v : V - 1)];
     }
     small_token_rows(topk_idx, topk_weights, T, k, E, R, cap, t, seg == 0, blockIdx.x == 0,
                      token_row, recv_src_idx, recv_w, expert_offset, rank_offset, recv_count, lds,

@@ -37,6 +37,7 @@
 //                 map token_rank_row instead of the [T, k] token_row
 #include "../../include/ep.h"
 #include "ep_device.h"
+#include "ep_ids.h"
 #include "ep_launch.h"
 
 namespace ep {
@@ -54,9 +55,12 @@ __device__ __forceinline__ int rank_of(int64_t e, int epr) {
 
 __device__ __forceinline__ uint64_t rank_mask(const int64_t* __restrict__ ids, int k, int E, int epr) {
     uint64_t m = 0;
-    for (int j = 0; j < k; ++j) {
-        const int64_t e = ids[j];
-        if (e >= 0 && e < E) m |= uint64_t(1) << rank_of(e, epr);
+    for (int j0 = 0; j0 < k; j0 += kIdBatch) {
+        int64_t v[kIdBatch];
+        load_ids(ids, j0, k, v);
+#pragma unroll
+        for (int u = 0; u < kIdBatch; ++u)
+            if (v[u] >= 0 && v[u] < E) m |= uint64_t(1) << rank_of(v[u], epr);
     }
     return m;
 }
@@ -76,6 +80,8 @@ __global__ __launch_bounds__(kHtTile) void ht_tile_hist_kernel(const int64_t* __
     if (threadIdx.x < R) hist[static_cast<int64_t>(blockIdx.x) * R + threadIdx.x] = h[threadIdx.x];
 }
 
+constexpr int kHtStageRanks = 32;
+constexpr int kHtStagePitch = kHtStageRanks + 1;
 __global__ __launch_bounds__(kHtTile) void ht_rows_kernel(
     const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, int ntiles,
     const int32_t* __restrict__ hist, int32_t* __restrict__ token_rank_row,
@@ -136,14 +142,30 @@ __global__ __launch_bounds__(kHtTile) void ht_rows_kernel(
         }
     }
     __syncthreads();
-    if (!in) return;
-    // Lanes past the last token have m == 0, so they add nothing to a ballot
-    // whether or not they take part in it.
-    for (int r = 0; r < R; ++r) {
-        const uint64_t b = ballot((m >> r) & 1);
-        int row = -1;
-        if ((m >> r) & 1) row = wcnt[wave][r] + __popcll(b & lanes_below());
-        token_rank_row[t * R + r] = row;
+    // Rows of the tile's tokens, up to 32 ranks at a time: ranked by ballot
+    // into LDS (row pitch 33 words: no bank conflicts), then written out in
+    // order, so the tile's part of token_rank_row (contiguous when R <= 32,
+    // 128-byte runs per token otherwise) is stored coalesced.  Lanes past the
+    // last token have m == 0 and add nothing to a ballot.
+    __shared__ int32_t stage[kHtTile * kHtStagePitch];
+    const int64_t t0 = static_cast<int64_t>(c) * kHtTile;
+    const int nt = static_cast<int>(T - t0 < kHtTile ? T - t0 : kHtTile);
+    for (int r0 = 0; r0 < R; r0 += kHtStageRanks) {
+        const int nr = R - r0 < kHtStageRanks ? R - r0 : kHtStageRanks;
+        for (int rr = 0; rr < nr; ++rr) {
+            const int r = r0 + rr;
+            const uint64_t b = ballot((m >> r) & 1);
+            int row = -1;
+            if ((m >> r) & 1) row = wcnt[wave][r] + __popcll(b & lanes_below());
+            stage[threadIdx.x * kHtStagePitch + rr] = row;
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < nt * nr; i += kHtTile) {
+            const int tl = i / nr;
+            const int rr = i - tl * nr;
+            token_rank_row[(t0 + tl) * R + r0 + rr] = stage[tl * kHtStagePitch + rr];
+        }
+        __syncthreads();
     }
 }
 
@@ -166,22 +188,29 @@ __global__ __launch_bounds__(256) void ht_meta_kernel(
         const uint32_t t = i / uk;
         const int j = static_cast<int>(i - t * uk);
         const int64_t* ids = topk_idx + static_cast<int64_t>(t) * k;
-        uint64_t m = 0;                       // ranks the token reaches (R <= 64)
-        for (int jj = 0; jj < k; ++jj) {
-            const int64_t e = ids[jj];
-            if (e >= 0 && e < E) m |= uint64_t(1) << rank_of(e, epr);
-        }
         const int64_t e = ids[j];
+        const float wraw = (recv_w && topk_weights) ? topk_weights[i] : 0.0f;
+        uint64_t m = rank_mask(ids, k, E, epr);          // ranks the token reaches (R <= 64)
         const int rj = (e >= 0 && e < E) ? rank_of(e, epr) : -1;
-        const float wj = (recv_w && topk_weights && rj >= 0) ? topk_weights[i] : 0.0f;
-        for (; m; m &= m - 1) {
-            const int r = __builtin_ctzll(m);
-            const int row = token_rank_row[static_cast<int64_t>(t) * R + r];
-            if (row < 0) continue;
-            const bool local = r == rj;
-            recv_topk_idx[static_cast<int64_t>(row) * k + j] = local ? e - static_cast<int64_t>(r) * epr : -1;
-            if (recv_w) recv_w[static_cast<int64_t>(row) * k + j] = local ? wj : 0.0f;
-            if (j == 0) recv_src_idx[row] = static_cast<int32_t>(t);
+        const int32_t* trr = token_rank_row + static_cast<int64_t>(t) * R;
+        while (m) {
+            // The rows of up to kIdBatch of the token's ranks, loaded together
+            // (rank 0 stands in for a missing one, and is not used).
+            int rr[kIdBatch], row[kIdBatch];
+#pragma unroll
+            for (int u = 0; u < kIdBatch; ++u) {
+                rr[u] = m ? __builtin_ctzll(m) : -1;
+                m &= m - 1;
+                row[u] = trr[rr[u] >= 0 ? rr[u] : 0];
+            }
+#pragma unroll
+            for (int u = 0; u < kIdBatch; ++u) {
+                if (rr[u] < 0 || row[u] < 0) continue;
+                const bool local = rr[u] == rj;
+                recv_topk_idx[static_cast<int64_t>(row[u]) * k + j] = local ? e - static_cast<int64_t>(rr[u]) * epr : -1;
+                if (recv_w) recv_w[static_cast<int64_t>(row[u]) * k + j] = local ? wraw : 0.0f;
+                if (j == 0) recv_src_idx[row[u]] = static_cast<int32_t>(t);
+            }
         }
     }
 }

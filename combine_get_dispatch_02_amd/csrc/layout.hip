@@ -15,6 +15,7 @@
 //   2. layout_reduce: one thread per output counter sums the per-block
 //      histograms (integer sums: the result does not depend on order).
 #include "ep_device.h"
+#include "ep_ids.h"
 #include "ep_launch.h"
 
 namespace ep {
@@ -45,12 +46,17 @@ __global__ __launch_bounds__(kLayoutTokensPerBlock) void layout_partial_kernel(
     uint64_t m = 0;  // ranks this token reaches (R <= 64)
     if (t < T) {
         const int64_t* row = topk_idx + t * k;
-        for (int j = 0; j < k; ++j) {
-            const int64_t e = row[j];
-            if (e >= 0 && e < E) {
-                atomicAdd(&h_e[e], 1);
-                // 0 <= e < E: a 32-bit division (64-bit is a long software sequence)
-                m |= uint64_t(1) << (static_cast<uint32_t>(e) / static_cast<uint32_t>(epr));
+        for (int j0 = 0; j0 < k; j0 += kIdBatch) {
+            int64_t v[kIdBatch];
+            load_ids(row, j0, k, v);
+#pragma unroll
+            for (int u = 0; u < kIdBatch; ++u) {
+                const int64_t e = v[u];
+                if (e >= 0 && e < E) {
+                    atomicAdd(&h_e[e], 1);
+                    // 0 <= e < E: a 32-bit division (64-bit is a long software sequence)
+                    m |= uint64_t(1) << (static_cast<uint32_t>(e) / static_cast<uint32_t>(epr));
+                }
             }
         }
     }
