@@ -55,11 +55,21 @@ __global__ __launch_bounds__(kIndexThreads) void tile_hist_kernel(
     __syncthreads();
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tile_tokens;
     const int nt = static_cast<int>(T - t0 < tile_tokens ? T - t0 : tile_tokens);
-    const int S = nt * k;
+    const int S = nt * k;                 // <= kMaxTileSlots = kSlotsPerLane * kIndexThreads
     const int64_t* ids = topk_idx + t0 * k;
-    for (int s = threadIdx.x; s < S; s += kIndexThreads) {
-        const int64_t e = ids[s];
-        if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+    // All of a thread's ids are requested before any is counted (indices
+    // clamped to the tile's last slot: no branch around a load, which would
+    // make the compiler wait for each in turn).
+    int64_t v[kSlotsPerLane];
+#pragma unroll
+    for (int i = 0; i < kSlotsPerLane; ++i) {
+        const int s = i * kIndexThreads + static_cast<int>(threadIdx.x);
+        v[i] = ids[s < S ? s : S - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < kSlotsPerLane; ++i) {
+        const int s = i * kIndexThreads + static_cast<int>(threadIdx.x);
+        if (s < S && v[i] >= 0 && v[i] < E) atomicAdd(&h[v[i]], 1);
     }
     __syncthreads();
     int32_t* out = hist + static_cast<int64_t>(blockIdx.x) * E;
