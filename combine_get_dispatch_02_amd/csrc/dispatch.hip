@@ -444,23 +444,37 @@ __global__ __launch_bounds__(512) void copy_bf16_kernel(const u32x4* __restrict_
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int64_t t = blockIdx.x / segs;
-    const int v0 = static_cast<int>(blockIdx.x - t * segs) * (kCopyVec * kWave) + lane;
+    const int seg = static_cast<int>(blockIdx.x - t * segs);
+    const int v0 = seg * (kCopyVec * kWave) + lane;
+    // The wave's first destination row (w < kb <= k) is requested together
+    // with x, so the two round trips overlap.
+    const int r0 = token_row[t * k + w];
     u32x4 val[kCopyVec];
 #pragma unroll
     for (int u = 0; u < kCopyVec; ++u) {
         const int v = v0 + u * kWave;
         if (v < V) val[u] = x[t * V + v];
     }
-    for (int j = w; j < k; j += kb) {
-        const int r = token_row[t * k + j];
-        if (r < 0 || r >= num_rows) continue;
+    // A segment wholly inside the row is stored without a per-lane guard: a
+    // branch around each store made the compiler wait for the previous store
+    // to complete before issuing the next.
+    const bool full = (seg + 1) * (kCopyVec * kWave) <= V;
+    auto store_row = [&](int r) {
+        if (r < 0 || r >= num_rows) return;
         u32x4* dst = recv + static_cast<int64_t>(r) * V;
+        if (full) {
 #pragma unroll
-        for (int u = 0; u < kCopyVec; ++u) {
-            const int v = v0 + u * kWave;
-            if (v < V) __builtin_nontemporal_store(val[u], dst + v);
+            for (int u = 0; u < kCopyVec; ++u) __builtin_nontemporal_store(val[u], dst + v0 + u * kWave);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kCopyVec; ++u) {
+                const int v = v0 + u * kWave;
+                if (v < V) __builtin_nontemporal_store(val[u], dst + v);
+            }
         }
-    }
+    };
+    store_row(r0);
+    for (int j = w + kb; j < k; j += kb) store_row(token_row[t * k + j]);
 }
 
 // Quantise the 16 consecutive bf16 channels a lane holds (two 16-byte
@@ -516,6 +530,10 @@ __global__ __launch_bounds__(256) void copy_fp8_kernel(const u32x4* __restrict__
         const int64_t t = tile / tiles_per_token;
         const int ch0 = static_cast<int>(tile - t * tiles_per_token) * 1024 + lane * 16;
         const bool active = ch0 < H;
+        // The token's rows are requested together with x (lane j < k holds
+        // row j; the index is clamped, not branched on, so the load does not
+        // wait for x).
+        int my_row = token_row[t * k + (lane < k ? lane : k - 1)];
         u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
         if (active) {
             const u32x4* src = x + t * V + ch0 / 8;
@@ -524,8 +542,7 @@ __global__ __launch_bounds__(256) void copy_fp8_kernel(const u32x4* __restrict__
         }
         float s;
         const u32x4 q = quantize16(a0, a1, s);
-        int my_row = lane < k ? token_row[t * k + lane] : -1;
-        if (my_row >= num_rows) my_row = -1;
+        if (lane >= k || my_row >= num_rows) my_row = -1;
         for (int j = 0; j < k; ++j) {
             const int r = read_lane(my_row, j);
             if (r < 0) continue;
