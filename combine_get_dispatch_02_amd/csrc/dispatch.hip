@@ -716,14 +716,22 @@ __global__ __launch_bounds__(512) void dispatch_small_bf16_kernel(
     small_token_rows(topk_idx, topk_weights, T, k, E, R, cap, t, seg == 0, blockIdx.x == 0,
                      token_row, recv_src_idx, recv_w, expert_offset, rank_offset, recv_count, lds,
                      rows);
+    // A segment wholly inside the row is stored without a per-lane guard (a
+    // branch around each store makes the compiler wait for the one before).
+    const bool full = (seg + 1) * (kCopyVec * kWave) <= V;
     for (int j = w; j < k; j += kb) {
         const int r = rows[j];
         if (r < 0) continue;
         u32x4* dst = recv + static_cast<int64_t>(r) * V;
+        if (full) {
 #pragma unroll
-        for (int u = 0; u < kCopyVec; ++u) {
-            const int v = v0 + u * kWave;
-            if (v < V) __builtin_nontemporal_store(val[u], dst + v);
+            for (int u = 0; u < kCopyVec; ++u) __builtin_nontemporal_store(val[u], dst + v0 + u * kWave);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kCopyVec; ++u) {
+                const int v = v0 + u * kWave;
+                if (v < V) __builtin_nontemporal_store(val[u], dst + v);
+            }
         }
     }
 }
