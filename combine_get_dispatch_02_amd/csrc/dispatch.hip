@@ -289,8 +289,8 @@ __global__ __launch_bounds__(kIndexThreads) void rows_kernel(
 // instead of HBM (x is still read from HBM exactly once).
 constexpr int kFusedWeights = kMaxTileSlots / kFusedThreads;
 
-// One id of the sweep: counted in LDS as before or inside the tile (pre /
-// rest), and kept in LDS when it belongs to the tile.
+// One id of the sweep: counted in LDS among the slots before the tile (pre)
+// or the others (rest), and kept in LDS when it belongs to the tile.
 __device__ __forceinline__ void sweep_count(int64_t v, unsigned sl, unsigned lo, unsigned hi, int E,
                                             int32_t* pre, int32_t* rest, int32_t* tile_ids) {
     const bool valid = v >= 0 && v < E;
