@@ -7,6 +7,8 @@
 // receive buffer: one row per (token t, rank r) with t routed to r, ordered by
 // rank and then token.
 //
+// Up to 2048 slots (T * k) and 512 tokens: one launch (ht_small, index and
+// copy per (token, segment) block, as the packed small-batch dispatch).
 // Up to 16384 tokens, 16 ranks and top-16: two launches, deterministic, no
 // global atomics:
 //   ht_fused      one block of 1024 threads per 64-token tile: every block
@@ -362,6 +364,111 @@ __global__ __launch_bounds__(kHtFusedThreads) void ht_fused_kernel(
     }
 }
 
+// Small batches (T * k <= kSmallSlots): index and copy in one launch.  One
+// block per (token t, 2 KB column segment), as in the packed small-batch
+// dispatch.  Every block counts the rank masks of all tokens (one token per
+// thread, one ballot per rank per wave) into per-rank totals and the counts
+// of the tokens before t; a 64-lane scan over ranks gives recv_rank_offset
+// and t's row in each rank it reaches.  Wave w copies x[t]'s segment to the
+// rows of ranks w, w + 8, ...; the token's first block writes its
+// token_rank_row entries and the records of its rows; block 0 writes the
+// offsets.  The x segment and the ids are requested before anything waits.
+constexpr int kHtSmallThreads = 512;
+constexpr int kHtSmallWaves = kHtSmallThreads / kWave;
+__global__ __launch_bounds__(kHtSmallThreads) void ht_small_kernel(
+    const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_weights, int64_t T, int k, int E, int R, int V, int segs,
+    u32x4* __restrict__ recv, int32_t* __restrict__ token_rank_row,
+    int32_t* __restrict__ recv_src_idx, int64_t* __restrict__ recv_topk_idx,
+    float* __restrict__ recv_w, int32_t* __restrict__ rank_offset) {
+    __shared__ int32_t cnt_all[kHtSmallWaves][EP_MAX_RANKS];
+    __shared__ int32_t cnt_pre[kHtSmallWaves][EP_MAX_RANKS];
+    __shared__ int32_t rows[EP_MAX_RANKS];
+    __shared__ uint64_t tok_mask;
+    const int tid = static_cast<int>(threadIdx.x);
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int64_t t = blockIdx.x / segs;
+    const int seg = static_cast<int>(blockIdx.x - t * segs);
+    const int v0 = seg * (kCopyVec * kWave) + lane;
+    const int epr = E / R;
+    u32x4 val[kCopyVec];
+#pragma unroll
+    for (int u = 0; u < kCopyVec; ++u) {
+        const int v = v0 + u * kWave;
+        val[u] = x[t * V + (v < V ? v : V - 1)];
+    }
+    // Sweep: thread i takes token i (T <= kHtSmallThreads).
+    const uint64_t m = tid < T ? rank_mask(topk_idx + static_cast<int64_t>(tid) * k, k, E, epr) : 0;
+    int my_all = 0, my_pre = 0;
+    for (int r = 0; r < R; ++r) {
+        const bool bit = (m >> r) & 1u;
+        const int a = __popcll(ballot(bit));
+        const int p = __popcll(ballot(bit && tid < t));
+        if (lane == r) {
+            my_all = a;
+            my_pre = p;
+        }
+    }
+    if (lane < R) {
+        cnt_all[wave][lane] = my_all;
+        cnt_pre[wave][lane] = my_pre;
+    }
+    if (tid == t) tok_mask = m;
+    __syncthreads();
+    if (wave == 0) {
+        int tot = 0, pre = 0;
+        if (lane < R)
+            for (int w = 0; w < kHtSmallWaves; ++w) {
+                tot += cnt_all[w][lane];
+                pre += cnt_pre[w][lane];
+            }
+        int incl = tot;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int u = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += u;
+        }
+        const int excl = incl - tot;
+        if (blockIdx.x == 0) {
+            if (lane < R) rank_offset[lane] = excl;
+            if (lane == R - 1) rank_offset[R] = incl;
+        }
+        if (lane < R) rows[lane] = ((tok_mask >> lane) & 1u) ? excl + pre : -1;
+    }
+    __syncthreads();
+    const bool full = (seg + 1) * (kCopyVec * kWave) <= V;
+    for (int r = wave; r < R; r += kHtSmallWaves) {
+        const int row = rows[r];
+        if (row < 0) continue;
+        u32x4* dst = recv + static_cast<int64_t>(row) * V;
+        if (full) {
+#pragma unroll
+            for (int u = 0; u < kCopyVec; ++u) __builtin_nontemporal_store(val[u], dst + v0 + u * kWave);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kCopyVec; ++u) {
+                const int v = v0 + u * kWave;
+                if (v < V) __builtin_nontemporal_store(val[u], dst + v);
+            }
+        }
+    }
+    if (seg != 0) return;
+    if (tid < R) token_rank_row[t * R + tid] = rows[tid];
+    const bool want_w = recv_w != nullptr && topk_weights != nullptr;
+    for (int c = tid; c < R * k; c += kHtSmallThreads) {
+        const int r = c / k;
+        const int j = c - r * k;
+        const int row = rows[r];
+        if (row < 0) continue;
+        const int64_t e = topk_idx[t * k + j];
+        const bool local = e >= 0 && e < E && rank_of(e, epr) == r;
+        recv_topk_idx[static_cast<int64_t>(row) * k + j] = local ? e - static_cast<int64_t>(r) * epr : -1;
+        if (recv_w) recv_w[static_cast<int64_t>(row) * k + j] = (local && want_w) ? topk_weights[t * k + j] : 0.0f;
+        if (j == 0) recv_src_idx[row] = static_cast<int32_t>(t);
+    }
+}
+
 __global__ void ht_zero_offsets_kernel(int32_t* rank_offset, int R) {
     if (static_cast<int>(threadIdx.x) <= R) rank_offset[threadIdx.x] = 0;
 }
@@ -380,6 +487,17 @@ hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const floa
                               hipStream_t stream) {
     if (T == 0) {
         hipLaunchKernelGGL(ht_zero_offsets_kernel, dim3(1), dim3(2 * kWave), 0, stream, rank_offset, R);
+        return hipGetLastError();
+    }
+    const int64_t small_segs = ceil_div(H / 8, kCopyVec * kWave);
+    if (T <= kHtSmallThreads && T * k <= kSmallSlots &&
+        T * small_segs * kHtSmallThreads <= kMaxLaunchThreads) {
+        const int V = H / 8;
+        const int segs = static_cast<int>(small_segs);
+        hipLaunchKernelGGL(ht_small_kernel, dim3(static_cast<unsigned>(T * segs)), dim3(kHtSmallThreads),
+                           0, stream, static_cast<const u32x4*>(x), topk_idx, topk_weights, T, k, E, R, V,
+                           segs, static_cast<u32x4*>(recv_x), token_rank_row, recv_src_idx,
+                           recv_topk_idx, recv_w, rank_offset);
         return hipGetLastError();
     }
     if (T <= kHtFusedMaxTokens && R <= kHtFusedMaxR && k <= kHtFusedMaxK) {

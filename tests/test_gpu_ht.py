@@ -122,6 +122,21 @@ def test_ht_parity_full_size(name):
 
 # One-launch index path (T <= 16384, R <= 16, k <= 16; top-k <= 8 and 9..16
 # instantiations) and the three-launch path beyond it, both sides of each limit.
+# One-launch small-batch path (T * k <= 2048, T <= 512), including 64 ranks, a
+# ragged column segment and the limits on either side.
+@pytest.mark.parametrize("T,k,E,R,H", [(1, 8, 64, 64, 1024), (30, 8, 128, 64, 1032), (256, 8, 256, 16, 136),
+                                       (512, 4, 32, 8, 64), (513, 3, 24, 8, 64), (204, 10, 40, 20, 256), (205, 10, 40, 20, 256),
+                                       (128, 16, 64, 8, 7168)])
+def test_ht_small_batch_path(T, k, E, R, H):
+    rng = np.random.default_rng(T * 7 + R)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int64)            # duplicates allowed
+    idx[rng.random((T, k)) < 0.1] = -1
+    x = rng.integers(0, 0x7F00, size=(T, H)).astype(np.uint16)
+    w = rng.random((T, k)).astype(np.float32)
+    run_case(x, idx, w, E, R)
+    run_case(x, idx, None, E, R)
+
+
 @pytest.mark.parametrize("T,k,E,R,H", [(1, 1, 1, 1, 8), (37, 3, 12, 6, 64), (300, 5, 24, 6, 136),
                                        (700, 8, 2048, 64, 16), (257, 16, 64, 64, 64),
                                        (300, 12, 48, 12, 128), (130, 16, 16, 16, 64),
