@@ -57,7 +57,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
             for (int jj = 0; jj < KB; ++jj) {
                 const int j = j0 + jj;
                 rows[jj] = j < k ? read_lane(my_row, j) : -1;
-                if (rows[jj] >= 0) {
+                if (U == 1) {
+                    // Small batches (latency-bound): every row's load is
+                    // issued unconditionally, so all KB rows are in flight
+                    // before any is waited on (a branch or select around each
+                    // row's load makes the compiler wait for it before the
+                    // next).  An empty slot reads row 0 of y -- or, when y has
+                    // no rows, the wave's own output segment, which only this
+                    // wave writes, after its loads -- and never accumulates
+                    // it; the vector index is clamped to the row (lanes past
+                    // its end store nothing).
+                    const u32x4* src = num_rows > 0 ? y + static_cast<int64_t>(rows[jj] >= 0 ? rows[jj] : 0) * V
+                                                    : out + t * V;
+                    val[jj][0] = __builtin_nontemporal_load(src + (v0 < V ? v0 : V - 1));
+                } else if (rows[jj] >= 0) {
+                    // Large batches: bound by the DRAM side of the scattered
+                    // reads, where one row in flight per wave measured faster
+                    // than all of them.
                     const u32x4* src = y + static_cast<int64_t>(rows[jj]) * V;
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
