@@ -43,13 +43,24 @@ constexpr int kFusedThreads = 1024;
 // shorter at 4096 x 8 slots than with 8-byte loads (14.5 vs 16.1 us by
 // kernel trace, x prefetch included); 4 or 16 pair loads were slower.
 constexpr int kFusedBatch = 8;
+// Two-launch receive order: up to this many slots the x prefetch is split
+// between the histogram and ranking launches.
+constexpr int64_t kSplitPrefetchSlots = int64_t(1) << 17;
 typedef long long i64x2 __attribute__((ext_vector_type(2)));
 
 // Per-tile expert histogram: hist[tile][e] = valid slots of the tile's tokens
 // routed to e (LDS atomics; integer sums do not depend on order).
+// Blocks past the tiles (if any) read part of x through the caches instead
+// (see prefetch_vectors).
 __global__ __launch_bounds__(kIndexThreads) void tile_hist_kernel(
     const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int tile_tokens,
-    int32_t* __restrict__ hist) {
+    int32_t* __restrict__ hist, int ntiles, const u32x4* __restrict__ pf_src, int64_t pf_vecs,
+    uint32_t* __restrict__ pf_sink) {
+    if (static_cast<int>(blockIdx.x) >= ntiles) {   // whole block: x prefetch only
+        prefetch_vectors<kIndexThreads>(pf_src, pf_vecs, static_cast<int>(blockIdx.x) - ntiles,
+                                        static_cast<int>(gridDim.x) - ntiles, pf_sink);
+        return;
+    }
     extern __shared__ int32_t h[];
     for (int e = threadIdx.x; e < E; e += kIndexThreads) h[e] = 0;
     __syncthreads();
@@ -830,15 +841,24 @@ hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weig
         return hipGetLastError();
     }
     int32_t* hist = static_cast<int32_t*>(workspace);
-    hipLaunchKernelGGL(tile_hist_kernel, dim3(ntiles), dim3(kIndexThreads),
-                       static_cast<size_t>(E) * sizeof(int32_t), stream, topk_idx, T, k, E, tt, hist);
+    // The x prefetch: up to kSplitPrefetchSlots slots, half of it rides on the
+    // histogram launch and half on the ranking launch (at 8192 x top-6 this
+    // made ep_dispatch 94.0 -> 91.8 us); above, the histogram launch has
+    // tiles of up to 4096 slots of its own and all of it goes with the
+    // ranking launch (at 32768 x top-8 the split measured 3 us slower).
+    const int64_t pf_a = T * k <= kSplitPrefetchSlots ? (pf_bytes / 2) / 16 * 16 : 0;
+    const int pf_blocks_a = pf_a > 0 ? 4 * prefetch_blocks(pf_a) : 0;
+    hipLaunchKernelGGL(tile_hist_kernel, dim3(ntiles + pf_blocks_a), dim3(kIndexThreads),
+                       static_cast<size_t>(E) * sizeof(int32_t), stream, topk_idx, T, k, E, tt, hist,
+                       ntiles, static_cast<const u32x4*>(x), pf_a / 16, pf_sink);
     const size_t lds = (static_cast<size_t>(1 + kIndexWaves) * E + kIndexWaves) * sizeof(int32_t);
-    // The ranking launch carries the x prefetch (in 256-thread blocks).
-    const int pf_blocks = pf_bytes > 0 ? 4 * prefetch_blocks(pf_bytes) : 0;
+    // The ranking launch carries the rest of the x prefetch (in 256-thread blocks).
+    const int64_t pf_b = pf_bytes - pf_a;
+    const int pf_blocks = pf_b > 0 ? 4 * prefetch_blocks(pf_b) : 0;
+    const u32x4* pf_src_b = pf_b > 0 ? reinterpret_cast<const u32x4*>(static_cast<const char*>(x) + pf_a) : nullptr;
     hipLaunchKernelGGL(rows_kernel, dim3(ntiles + pf_blocks), dim3(kIndexThreads), lds, stream, topk_idx,
                        w_in, T, k, E, R, tt, ntiles, nbits, hist, token_row, recv_src_idx, w_out,
-                       expert_offset, rank_offset, cap, recv_count, static_cast<const u32x4*>(x),
-                       pf_bytes / 16, pf_sink);
+                       expert_offset, rank_offset, cap, recv_count, pf_src_b, pf_b / 16, pf_sink);
     return hipGetLastError();
 }
 
