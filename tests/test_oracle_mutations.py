@@ -88,6 +88,7 @@ def _combine_pins():
         tc.test_random_experts_within_fma_chain_bound(name, mask)
     tc.test_masked_and_out_of_range_rows_skipped()
     tc.test_signed_zero_start()
+    tc.test_hand_computed_order_and_fma()
 
 
 MUTATIONS = {
@@ -140,6 +141,15 @@ MUTATIONS = {
     "combine_negzero_start": ("float acc = 0.0f;\n            for (int j = 0; j < k; ++j) {\n                int32_t row",
                               "float acc = -0.0f;\n            for (int j = 0; j < k; ++j) {\n                int32_t row",
                               _combine_pins),
+    "combine_reverse_j": ("for (int j = 0; j < k; ++j) {\n                int32_t row = token_row[t * k + j];\n                if (row < 0 || (int64_t)row >= num_rows) continue;",
+                          "for (int j = k - 1; j >= 0; --j) {\n                int32_t row = token_row[t * k + j];\n                if (row < 0 || (int64_t)row >= num_rows) continue;",
+                          _combine_pins),
+    "combine_mul_then_add": ("acc = fmaf(wj, bf16_to_f32(expert_out[(int64_t)row * H + h]), acc);",
+                             "{ float p = wj * bf16_to_f32(expert_out[(int64_t)row * H + h]); acc = acc + p; }",
+                             _combine_pins),
+    "combine_fp64_accumulator": ("float acc = 0.0f;\n            for (int j = 0; j < k; ++j) {\n                int32_t row = token_row[t * k + j];\n                if (row < 0 || (int64_t)row >= num_rows) continue;\n                const float wj = topk_weights ? topk_weights[t * k + j] : 1.0f;\n                acc = fmaf(wj, bf16_to_f32(expert_out[(int64_t)row * H + h]), acc);",
+                                 "double acc = 0.0;\n            for (int j = 0; j < k; ++j) {\n                int32_t row = token_row[t * k + j];\n                if (row < 0 || (int64_t)row >= num_rows) continue;\n                const float wj = topk_weights ? topk_weights[t * k + j] : 1.0f;\n                acc = fma((double)wj, (double)bf16_to_f32(expert_out[(int64_t)row * H + h]), acc);",
+                                 _combine_pins),
     "combine_no_range_guard": ("if (row < 0 || (int64_t)row >= num_rows) continue;\n                const float wj",
                                "if (row < 0) continue;\n                if (row >= num_rows) row = num_rows - 1;\n                const float wj",
                                _combine_pins),
