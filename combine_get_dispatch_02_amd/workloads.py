@@ -25,7 +25,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["Workload", "CONFIGS", "make_workload", "make_routing", "bf16_bits",
-           "random_bf16", "expert_outputs", "mask_slots"]
+           "random_bf16", "expert_outputs", "pooled_expert_outputs", "mask_slots"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -149,6 +149,18 @@ def expert_outputs(wl: Workload, rows: int, seed_extra: int = 0) -> np.ndarray:
     """Seeded stand-in expert outputs y[rows, H] (bf16 bits), N(0,1)."""
     rng = np.random.default_rng([2026, wl.cfg_id, 7, seed_extra])
     return random_bf16(rng, rows, wl.H, 1.0)
+
+
+def pooled_expert_outputs(wl: Workload, rows: int, pool_rows: int = 4096, seed_extra: int = 0):
+    """Seeded stand-in expert outputs for full-size batches, where drawing
+    rows x H normals would dominate a test: y[r] = pool[sel[r]] with pool
+    N(0,1) bf16 bits [pool_rows, H] and sel uniform over the pool.  Returns
+    (pool, sel), so each side can form y (or index the pool) without the host
+    holding rows x H values."""
+    rng = np.random.default_rng([2026, wl.cfg_id, 8, seed_extra])
+    pool = random_bf16(rng, pool_rows, wl.H, 1.0)
+    sel = rng.integers(0, pool_rows, size=rows).astype(np.int32)
+    return pool, sel
 
 
 def mask_slots(idx: np.ndarray, frac: float, seed: int = 0) -> np.ndarray:

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from combine_get_dispatch_02_amd.workloads import CONFIGS, make_workload
-from test_gpu_parity import fp8_ulp_ok
+from parity import assert_fp8_codes
 
 pytestmark = pytest.mark.gpu
 EXE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_caller", "ep_c_caller")
@@ -91,4 +91,4 @@ def test_c_caller_matches_oracle(case, tmp_path):
     np.testing.assert_array_equal(o["combined_x"], oracle.combine(ref["recv_x"], ref["token_row"], w))
     rf = oracle.dispatch_fp8(x, idx, w, wl.E, wl.R)
     np.testing.assert_array_equal(o["recv_scales"].view(np.uint32), rf["recv_scales"][:N].view(np.uint32))
-    assert fp8_ulp_ok(o["recv_x_fp8"], rf["recv_x_fp8"][:N])
+    assert_fp8_codes(o["recv_x_fp8"], rf["recv_x_fp8"][:N])

@@ -15,7 +15,9 @@ import torch
 import oracle
 from combine_get_dispatch_02_amd import ep
 from combine_get_dispatch_02_amd.workloads import CONFIGS, make_workload, mask_slots, random_bf16
-from test_gpu_parity import SENT16, SENT8, dev_bf16, fp8_ulp_ok, host_bits
+from parity import assert_combine, assert_fp8_codes
+from test_gpu_parity import (SENT16, SENT8, assert_rows_hold_token_casts, dev_bf16, host_bits,
+                              rows_as_tokens, token_casts)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -57,7 +59,7 @@ def run_case(x, idx, w, E, cap, fp8, y_rng=None):
     if fp8:
         q = d["recv_x_fp8"].cpu().numpy()
         s = d["recv_scales"].cpu().numpy()
-        assert fp8_ulp_ok(q[filled], ref["recv_x_fp8"][filled])
+        assert_fp8_codes(q[filled], ref["recv_x_fp8"][filled])
         np.testing.assert_array_equal(s[filled].view(np.uint32), ref["recv_scales"][filled].view(np.uint32))
         assert np.all(q[~filled] == SENT8) and np.all(np.isnan(s[~filled]))
     else:
@@ -135,9 +137,11 @@ def test_ll_empty_batch_and_all_empty_slots():
 def test_ll_full_size_ll_workload_and_dsv3():
     """The LL workload at full size (T=128, H=7168) at capacity T, and the dsv3
     workload (T=4096, H=7168, k=8, E=256) at capacity 256 (2x the mean load):
-    maps and counts bit-exact against the oracle (computed with H=128, since
-    they do not depend on H), rows checked against x / the oracle's cast of
-    sampled tokens."""
+    maps and counts bit-exact against the oracle (computed with H=8, since
+    they do not depend on H); every filled bf16 slot against x at the oracle's
+    source token, every filled FP8 slot against the oracle's cast of that
+    token, and the combine over token_slot of every token against the
+    oracle's."""
     for name, cap in (("ll_fp8", 128), ("dsv3", 256)):
         wl = CONFIGS[name]
         print(f"[ll-full] {wl.describe()} cap={cap}", flush=True)
@@ -152,15 +156,18 @@ def test_ll_full_size_ll_workload_and_dsv3():
         for o in (d, q):
             np.testing.assert_array_equal(o["token_slot"].cpu().numpy(), ref["token_slot"])
             np.testing.assert_array_equal(o["recv_count"].cpu().numpy(), ref["recv_count"])
-        filled = torch.from_numpy(ref["recv_src_idx"] >= 0).to(DEV)
-        src = torch.from_numpy(ref["recv_src_idx"].astype(np.int64)).to(DEV)
-        assert torch.equal(d["recv_src_idx"][filled], src[filled].to(torch.int32))
-        assert torch.equal(d["recv_x"][filled].view(torch.int16), xd[src[filled]].view(torch.int16))
-        slots = ref["token_slot"]
-        qh = q["recv_x_fp8"].view(wl.E * cap, wl.H)
-        sh = q["recv_scales"].view(wl.E * cap, wl.H // 128)
-        for t in np.random.default_rng(7).choice(wl.T, size=24, replace=False):
-            qt, st = oracle.quantize_row(x[t])
-            for sl in slots[t][slots[t] >= 0]:
-                assert fp8_ulp_ok(qh[sl].cpu().numpy(), qt)
-                np.testing.assert_array_equal(sh[sl].cpu().numpy().view(np.uint32), st.view(np.uint32))
+        src_all = ref["recv_src_idx"].ravel()
+        filled_rows = np.nonzero(src_all >= 0)[0]
+        src = src_all[filled_rows]
+        rows_d = torch.from_numpy(filled_rows.astype(np.int64)).to(DEV)
+        src_d = torch.from_numpy(src.astype(np.int64)).to(DEV)
+        assert torch.equal(d["recv_src_idx"].view(-1)[rows_d], src_d.to(torch.int32))
+        assert torch.equal(d["recv_x"].view(wl.E * cap, wl.H)[rows_d].view(torch.int16),
+                           xd[src_d].view(torch.int16))
+        qtok, stok = token_casts(x)
+        assert_rows_hold_token_casts(q["recv_x_fp8"].view(wl.E * cap, wl.H)[rows_d],
+                                     q["recv_scales"].view(wl.E * cap, wl.H // 128)[rows_d],
+                                     src, qtok, stok, f"{name} padded fp8")
+        got = host_bits(ep.ep_combine(d["recv_x"].view(wl.E * cap, wl.H), d["token_slot"], wd))
+        assert_combine(got, oracle.combine(x, rows_as_tokens(ref["token_slot"], src_all), w),
+                       f"{name} combine over token_slot")

@@ -25,7 +25,8 @@ import torch
 
 import oracle
 from combine_get_dispatch_02_amd import ep
-from test_gpu_parity import fp8_ulp_ok, host_bits
+from parity import assert_fp8_codes
+from test_gpu_parity import host_bits
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -105,7 +106,7 @@ def test_largest_batch_one_launch_accepts():
     for t in samples[:64]:
         qt, st = oracle.quantize_row(host_bits(xd[int(t)]))
         for r in token_row[t][token_row[t] >= 0]:
-            assert fp8_ulp_ok(f["recv_x_fp8"][int(r)].cpu().numpy(), qt)
+            assert_fp8_codes(f["recv_x_fp8"][int(r)].cpu().numpy(), qt)
             np.testing.assert_array_equal(f["recv_scales"][int(r)].cpu().numpy().view(np.uint32),
                                           st.view(np.uint32))
     del f

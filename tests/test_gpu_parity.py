@@ -1,16 +1,19 @@
 """GPU parity: the HIP path (through the C ABI of libep.so) against the CPU
 oracle, on seeded synthetic inputs.
 
-Bar: layout, offsets, token_row, recv_src_idx, recv_topk_weights and
-dispatched bytes bit-exact; FP8 scales bit-exact and codes within 1 ulp
-(same sign, magnitude ordinals differ by <= 1); combine within max relative
-error 8e-3 (bf16 output) -- and, because both sides run the same fp32 fma
-chain in the same order, bit-exact, checked separately at the end.
+Bars (tests/parity.py): layout, offsets, token_row, recv_src_idx,
+recv_topk_weights and dispatched bytes bit-exact; FP8 scales bit-exact and
+codes identical (the stated tolerance is one code step, never a NaN code for
+a finite one; both sides divide in IEEE fp32, so the codes are identical);
+combine within max relative error 8e-3 and, because both sides run the same
+fp32 fma chain in slot order, bit-exact.
 
 Oracle-sized cases compare every output element.  Full-size workloads (the
-launch shapes the benchmark times) compare the layout and every index map in
-full, every dispatched row against x at the oracle's source index, and
-combine on sampled tokens recomputed by the oracle.
+launch shapes the benchmark times) compare every output as well: the layout
+and every index map against the oracle, every dispatched row against x at the
+oracle's source index, every FP8 row against the oracle's cast of its token,
+and every combined token against the oracle's combine (identity experts, and
+seeded distinct expert outputs with signed weights).
 """
 import dataclasses
 
@@ -20,13 +23,14 @@ import torch
 
 import oracle
 from combine_get_dispatch_02_amd import ep
-from combine_get_dispatch_02_amd.workloads import CONFIGS, expert_outputs, make_workload, mask_slots, random_bf16
+from combine_get_dispatch_02_amd.workloads import (CONFIGS, expert_outputs, make_workload, mask_slots,
+                                                   pooled_expert_outputs, random_bf16)
+from parity import assert_combine, assert_fp8_codes, f32  # noqa: F401  (f32 re-exported)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 SENT16 = 0x7FBF       # bf16 sentinel (a NaN pattern no path writes)
 SENT8 = 0xA5
-COMBINE_RTOL = 8e-3
 
 
 def dev_bf16(a):
@@ -37,25 +41,8 @@ def host_bits(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def f32(bits):
-    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32)
-
-
 def _say(msg):
     print(msg, flush=True)
-
-
-def combine_rel_err(got_bits, ref_bits):
-    g, r = f32(got_bits).astype(np.float64), f32(ref_bits).astype(np.float64)
-    return float(np.max(np.abs(g - r) / np.maximum(np.abs(r), 1e-6))) if r.size else 0.0
-
-
-def fp8_ulp_ok(got, ref):
-    got, ref = got.astype(np.int32), ref.astype(np.int32)
-    same_sign = ((got ^ ref) & 0x80) == 0
-    either_zero = ((got & 0x7F) == 0) | ((ref & 0x7F) == 0)
-    close = np.abs((got & 0x7F) - (ref & 0x7F)) <= 1
-    return bool(np.all(close & (same_sign | either_zero)))
 
 
 def gpu_layout(idx_d, wl):
@@ -145,8 +132,7 @@ def test_parity_oracle_sized(case):
     for yy, tag in ((y, "random"), (ref_d["recv_x"], "identity")):
         ref_c = oracle.combine(yy, ref_d["token_row"], w, num_rows=N)
         got = host_bits(ep.ep_combine(dev_bf16(yy), d["token_row"], wd, num_rows=N))
-        err = combine_rel_err(got, ref_c)
-        assert err <= COMBINE_RTOL, (tag, err)
+        assert_combine(got, ref_c, tag)
 
     if H % 128 == 0:
         ref_f = oracle.dispatch_fp8(x, idx, w, wl.E, wl.R)
@@ -157,13 +143,47 @@ def test_parity_oracle_sized(case):
         q = f["recv_x_fp8"].cpu().numpy()
         s = f["recv_scales"].cpu().numpy()
         np.testing.assert_array_equal(s[:N].view(np.uint32), ref_f["recv_scales"][:N].view(np.uint32))
-        assert fp8_ulp_ok(q[:N], ref_f["recv_x_fp8"][:N])
+        assert_fp8_codes(q[:N], ref_f["recv_x_fp8"][:N])
         assert np.all(q[N:] == SENT8) and np.all(np.isnan(s[N:]))
 
 
 # --------------------------------------------------------------------------
 # Full-size workloads, in the launch shapes that the benchmark times.
 FULL = ["tiny", "dsv3", "skewed", "ll_fp8", "large"]
+
+
+def token_casts(x):
+    """The oracle's FP8 cast of every token once: (codes [T,H], scales [T,H/128])
+    -- its cached dispatch over the map that sends token t to row t."""
+    T = x.shape[0]
+    return oracle.dispatch_fp8_cached(x, np.arange(T, dtype=np.int32)[:, None], T)
+
+
+def assert_rows_hold_token_casts(q_d, s_d, src, qtok, stok, what):
+    """Every receive row r: codes and scales equal the oracle's cast of token
+    src[r] (compared on the device, 64K rows at a time; the first mismatching
+    chunk is brought back for the report)."""
+    qtok_d = torch.from_numpy(qtok).to(DEV)
+    stok_d = torch.from_numpy(stok.view(np.int32)).to(DEV)
+    src_d = torch.from_numpy(np.asarray(src, np.int64)).to(DEV)
+    n = src_d.numel()
+    for r0 in range(0, n, 65536):
+        r1 = min(n, r0 + 65536)
+        sel = src_d[r0:r1]
+        ok_q = torch.equal(q_d[r0:r1], qtok_d[sel])
+        ok_s = torch.equal(s_d[r0:r1].view(torch.int32), stok_d[sel])
+        if not (ok_q and ok_s):
+            sh = src[r0:r1]
+            np.testing.assert_array_equal(s_d[r0:r1].cpu().numpy().view(np.uint32),
+                                          stok[sh].view(np.uint32), err_msg=f"{what} scales rows {r0}..{r1}")
+            assert_fp8_codes(q_d[r0:r1].cpu().numpy(), qtok[sh], f"{what} codes rows {r0}..{r1}")
+
+
+def rows_as_tokens(token_row, src):
+    """The map that reads, for slot (t, j), the token whose bits its receive row
+    holds: src[token_row[t, j]], -1 kept.  Combine over identity experts (y =
+    the dispatched rows) then equals combine over x with this map."""
+    return np.where(token_row >= 0, src[np.maximum(token_row, 0)], -1).astype(np.int32)
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -177,6 +197,7 @@ def test_parity_full_size(name):
     ref_d = oracle.dispatch(np.ascontiguousarray(x[:, :8]), idx, w, wl.E, wl.R)
     N = int(ref_d["recv_expert_offset"][-1])
     assert N == T * k
+    src = ref_d["recv_src_idx"][:N]
 
     xd, idxd, wd = dev_bf16(x), torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV)
     check_layout(gpu_layout(idxd, wl), ref_l)
@@ -184,42 +205,37 @@ def test_parity_full_size(name):
     torch.cuda.synchronize()
     check_index_maps(d, ref_d, N)
     # every dispatched row equals x at the oracle's source index, bit for bit
-    src = torch.from_numpy(ref_d["recv_src_idx"][:N].astype(np.int64)).to(DEV)
+    src_d = torch.from_numpy(src.astype(np.int64)).to(DEV)
     for r0 in range(0, N, 65536):
         r1 = min(N, r0 + 65536)
-        assert torch.equal(d["recv_x"][r0:r1].view(torch.int16), xd[src[r0:r1]].view(torch.int16)), (r0, r1)
+        assert torch.equal(d["recv_x"][r0:r1].view(torch.int16), xd[src_d[r0:r1]].view(torch.int16)), (r0, r1)
+    del src_d
 
-    # combine over all tokens on the GPU; oracle recomputes sampled tokens
-    rng = np.random.default_rng(123)
-    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=min(T, 48), replace=False)]))
-    if T * H <= 4096 * 7168:
-        y = expert_outputs(wl, N)
-        yd = dev_bf16(y)
-    else:                    # identity experts: the dispatched rows themselves
-        y, yd = None, d["recv_x"]
-    got = host_bits(ep.ep_combine(yd, d["token_row"], wd, num_rows=N))
-    trow = ref_d["token_row"][toks]
-    if y is None:
-        rows_y = np.repeat(x[toks], k, axis=0)                     # row (i, j) = x[t_i]
-    else:
-        rows_y = y[trow.ravel()]
-    local = np.arange(len(toks) * k, dtype=np.int32).reshape(len(toks), k)
-    ref_c = oracle.combine(rows_y, local, w[toks])
-    err = combine_rel_err(got[toks], ref_c)
-    assert err <= COMBINE_RTOL, err
+    # combine over every token, (1) identity experts with the softmax weights
+    # (the benchmark's case): y = the dispatched rows, whose row r holds x[src[r]]
+    got = host_bits(ep.ep_combine(d["recv_x"], d["token_row"], wd, num_rows=N))
+    assert_combine(got, oracle.combine(x, rows_as_tokens(ref_d["token_row"], src), w), "identity experts")
+    # (2) distinct seeded expert outputs y[r] = pool[sel[r]] and signed random
+    # weights, so that a weight paired with the wrong slot, a wrong row or a
+    # lost cancellation shows
+    pool, sel = pooled_expert_outputs(wl, N)
+    w2 = np.random.default_rng(17).standard_normal(w.shape).astype(np.float32)
+    yd = dev_bf16(pool)[torch.from_numpy(sel.astype(np.int64)).to(DEV)]
+    got = host_bits(ep.ep_combine(yd, d["token_row"], torch.from_numpy(w2).to(DEV), num_rows=N))
+    del yd
+    sel_map = np.where(ref_d["token_row"] >= 0, sel[np.maximum(ref_d["token_row"], 0)], -1).astype(np.int32)
+    assert_combine(got, oracle.combine(pool, sel_map, w2), "pooled expert outputs")
+    del d
+    torch.cuda.empty_cache()
 
-    if wl.fp8 or name == "dsv3":
-        out = prefilled_dispatch_out(T, k, H, wl.E, wl.R, fp8=True)
-        f = ep.ep_dispatch_fp8(xd, idxd, wd, wl.E, wl.R, out=out)
-        torch.cuda.synchronize()
-        check_index_maps(f, ref_d, N)
-        q = f["recv_x_fp8"].cpu().numpy()
-        s = f["recv_scales"].cpu().numpy()
-        for t in toks:
-            qr, sr = oracle.quantize_row(x[t])
-            for r in ref_d["token_row"][t]:
-                np.testing.assert_array_equal(s[r].view(np.uint32), sr.view(np.uint32))
-                assert fp8_ulp_ok(q[r], qr)
+    # FP8 dispatch: maps again, and every row against the oracle's cast of its token
+    out = prefilled_dispatch_out(T, k, H, wl.E, wl.R, fp8=True)
+    f = ep.ep_dispatch_fp8(xd, idxd, wd, wl.E, wl.R, out=out)
+    torch.cuda.synchronize()
+    check_index_maps(f, ref_d, N)
+    qtok, stok = token_casts(x)
+    assert_rows_hold_token_casts(f["recv_x_fp8"], f["recv_scales"], src, qtok, stok, "fp8 dispatch")
+    assert bool((f["recv_x_fp8"][N:] == SENT8).all()) and bool(torch.isnan(f["recv_scales"][N:]).all())
 
 
 # --------------------------------------------------------------------------
@@ -320,7 +336,7 @@ def test_fp8_dispatch_paths(T, k, E, R, H):
     q = f["recv_x_fp8"].cpu().numpy()
     sc = f["recv_scales"].cpu().numpy()
     np.testing.assert_array_equal(sc[:N].view(np.uint32), ref["recv_scales"][:N].view(np.uint32))
-    assert fp8_ulp_ok(q[:N], ref["recv_x_fp8"][:N])
+    assert_fp8_codes(q[:N], ref["recv_x_fp8"][:N])
     assert np.all(q[N:] == SENT8)
 
 
