@@ -281,8 +281,14 @@ int ep_dispatch_ll_fp8(const void* x, const int64_t* topk_idx, const float* topk
  * order), which is the combine of ep_dispatch_ht's per-rank rows.
  *
  *   expert_out   [num_rows, H] bf16 in (16-byte aligned)
- *   token_row    [T, k]        int32 in (from ep_dispatch; rows outside
- *                              [0, num_rows) are skipped, never read)
+ *   token_row    [T, k]        int32 in (from ep_dispatch; a slot whose row
+ *                              lies outside [0, num_rows) contributes nothing.
+ *                              For small batches the kernel still issues a
+ *                              load for such a slot -- of row 0 of expert_out,
+ *                              or, when num_rows == 0, of the token's own
+ *                              combined_x segment before writing it -- and
+ *                              discards the value; nothing outside the
+ *                              buffers described here is read)
  *   topk_weights [T, k]        fp32  in (NULL: all weights 1)
  *   combined_x   [T, H]        bf16  out (16-byte aligned)
  * Requires H % 8 == 0, 1 <= k <= EP_MAX_TOPK, num_rows >= 0.  No workspace.
