@@ -524,6 +524,28 @@ def test_combine_bit_exact_fma_chain(name):
         np.testing.assert_array_equal(got, ref_c)
 
 
+@pytest.mark.parametrize("T,H", [(5, 8), (600, 1032), (4096, 1024)],
+                         ids=["golden", "one-vector", "two-vector"])
+def test_combine_order_golden(T, H):
+    """The hand-worked cases of tests/golden/combine_order.json (their answers
+    change with the slot order, the fusion and the grouping of the sum),
+    repeated over T tokens and H channels: the (4096, 1024) shape takes the
+    two-vector combine kernel that the full-size batches use, the others the
+    one-vector kernel."""
+    from test_oracle_combine import _load_order_golden
+    y, trow, w, exp_bits, _, H0 = _load_order_golden()
+    n = trow.shape[0]
+    y = np.ascontiguousarray(np.repeat(y[:, :1], H, axis=1))
+    tok = np.arange(T) % n
+    trow_t = np.ascontiguousarray(trow[tok])
+    w_t = np.ascontiguousarray(w[tok])
+    got = host_bits(ep.ep_combine(dev_bf16(y), torch.from_numpy(trow_t).to(DEV),
+                                  torch.from_numpy(w_t).to(DEV), num_rows=y.shape[0]))
+    expect = np.repeat(exp_bits[tok][:, None], H, axis=1)
+    assert_combine(got, expect, "golden")
+    assert_combine(got, oracle.combine(y, trow_t, w_t), "oracle")
+
+
 def test_binding_rejects_wrong_outputs():
     """Caller-supplied outputs are checked before the raw pointers reach the
     kernels: a smaller, mistyped or misplaced tensor raises, nothing runs."""
