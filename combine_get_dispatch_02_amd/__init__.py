@@ -8,10 +8,11 @@ workload generator (:mod:`.workloads`).
 from .ep import (EPError, ep_combine, ep_dispatch, ep_dispatch_cached,  # noqa: F401
                  ep_dispatch_fp8, ep_dispatch_fp8_cached, ep_dispatch_ht,
                  ep_dispatch_ht_workspace_bytes, ep_dispatch_ll, ep_dispatch_ll_fp8,
-                 ep_dispatch_ll_workspace_bytes, ep_dispatch_workspace_bytes,
+                 ep_dispatch_ll_workspace_bytes, ep_dispatch_noalloc, ep_dispatch_workspace_bytes,
                  ep_get_dispatch_layout, ep_layout_workspace_bytes, lib, version)
 
-__all__ = ["EPError", "ep_get_dispatch_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_combine",
+__all__ = ["EPError", "ep_get_dispatch_layout", "ep_dispatch", "ep_dispatch_noalloc", "ep_dispatch_fp8",
+           "ep_combine",
            "ep_dispatch_cached", "ep_dispatch_fp8_cached", "ep_dispatch_ht",
            "ep_dispatch_ht_workspace_bytes", "ep_dispatch_ll", "ep_dispatch_ll_fp8",
            "ep_dispatch_ll_workspace_bytes",

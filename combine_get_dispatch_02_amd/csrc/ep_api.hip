@@ -7,6 +7,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/ep.h"
 #include "ep_launch.h"
 
@@ -53,10 +55,9 @@ int check_workspace(const char* fn, int64_t T, const void* ws, size_t ws_bytes, 
     return EP_OK;
 }
 
-int check_dispatch_common(const char* fn, const void* x, const int64_t* topk_idx, int64_t T,
-                          int H, int k, int E, int R, const void* recv, const int32_t* recv_src_idx,
-                          const int32_t* expert_offset, const int32_t* token_row, const void* ws,
-                          size_t ws_bytes) {
+int check_dispatch_args(const char* fn, const void* x, const int64_t* topk_idx, int64_t T, int H,
+                        int k, int E, int R, const void* recv, const int32_t* recv_src_idx,
+                        const int32_t* expert_offset, const int32_t* token_row) {
     int s = check_routing(fn, topk_idx, T, k, E, R);
     if (s != EP_OK) return s;
     if (H < 8 || H % 8 != 0) return fail(EP_ERR_INVALID_ARGUMENT, "%s: hidden must be a positive multiple of 8", fn);
@@ -65,7 +66,88 @@ int check_dispatch_common(const char* fn, const void* x, const int64_t* topk_idx
         return fail(EP_ERR_INVALID_ARGUMENT, "%s: a required pointer is NULL", fn);
     if (T > 0 && (!aligned16(x) || !aligned16(recv)))
         return fail(EP_ERR_INVALID_ARGUMENT, "%s: x and the receive buffer must be 16-byte aligned", fn);
+    return EP_OK;
+}
+
+int check_dispatch_common(const char* fn, const void* x, const int64_t* topk_idx, int64_t T,
+                          int H, int k, int E, int R, const void* recv, const int32_t* recv_src_idx,
+                          const int32_t* expert_offset, const int32_t* token_row, const void* ws,
+                          size_t ws_bytes) {
+    int s = check_dispatch_args(fn, x, topk_idx, T, H, k, E, R, recv, recv_src_idx, expert_offset,
+                                token_row);
+    if (s != EP_OK) return s;
     return check_workspace(fn, T, ws, ws_bytes, ep::index_workspace_bytes(T, k, E));
+}
+
+// The launch sequence of ep_dispatch (arguments already validated): small
+// batches in one launch, else the receive-order launch(es) then the copy.
+int dispatch_bf16(const char* fn, const void* x, const int64_t* topk_idx, const float* topk_weights,
+                  int64_t T, int H, int k, int E, int R, void* recv_x, int32_t* recv_src_idx,
+                  float* recv_w, int32_t* expert_offset, int32_t* rank_offset, int32_t* token_row,
+                  void* workspace, hipStream_t st) {
+    if (!ep::copy_launch_fits(T, H, k))
+        return fail(EP_ERR_UNSUPPORTED, "%s: num_tokens * hidden too large for one copy launch", fn);
+    if (ep::dispatch_is_small(T, k))
+        return hip_status(ep::launch_dispatch_small_bf16(x, topk_idx, topk_weights, T, H, k, E, R, 0,
+                                                         recv_x, recv_src_idx, recv_w, expert_offset,
+                                                         rank_offset, nullptr, token_row, st),
+                          fn);
+    int s = hip_status(ep::launch_dispatch_index(topk_idx, topk_weights, T, k, E, R, recv_src_idx,
+                                                 recv_w, expert_offset, rank_offset, token_row,
+                                                 workspace, x, T * static_cast<int64_t>(H) * 2, 0,
+                                                 nullptr, st),
+                       fn);
+    if (s != EP_OK) return s;
+    return hip_status(ep::launch_dispatch_copy_bf16(x, token_row, recv_x, T * k, T, H, k, st), fn);
+}
+
+// ---- fixed device scratch of ep_dispatch_noalloc ------------------------------
+// For callers that cannot allocate, the receive-order scratch of ep_dispatch
+// lives in the file-scope array `scratch` below: kScratchBytes per GPU, held
+// until the process ends.  On the host the array's name is only a stand-in,
+// not a device address; host code uses the address hipGetSymbolAddress
+// returns for the current device, looked up once per device and kept in
+// g_scratch.  Nothing in it must start at zero: the receive-order kernels
+// write every histogram word they later read, and the prefetch words are
+// write-only.  Calls that overlap on one GPU share the array and race.
+constexpr size_t kScratchBytes = EP_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxScratchDevices];
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// This device's address of `scratch`; the stream must belong to the current
+// device (the array's address differs per device).
+int scratch_for_stream(const char* fn, hipStream_t st, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(EP_ERR_UNSUPPORTED, "%s: device %d beyond the %d the scratch table holds", fn, dev,
+                    kMaxScratchDevices);
+    if (st) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(st, &sdev);
+        if (e != hipSuccess) return hip_status(e, fn);
+        if (sdev != dev)
+            return fail(EP_ERR_INVALID_ARGUMENT, "%s: the stream belongs to device %d, the current device is %d",
+                        fn, static_cast<int>(sdev), dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, fn);
+        if (!p) return fail(EP_ERR_HIP, "%s: no device address for the scratch array", fn);
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return EP_OK;
 }
 
 }  // namespace
@@ -133,27 +215,35 @@ int ep_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weight
                                   num_ranks, recv_x, recv_src_idx, recv_expert_offset, token_row,
                                   workspace, workspace_bytes);
     if (s != EP_OK) return s;
-    if (!ep::copy_launch_fits(num_tokens, hidden, num_topk))
-        return fail(EP_ERR_UNSUPPORTED, "%s: num_tokens * hidden too large for one copy launch", fn);
+    return dispatch_bf16(fn, x, topk_idx, topk_weights, num_tokens, hidden, num_topk, num_experts,
+                         num_ranks, recv_x, recv_src_idx, recv_topk_weights, recv_expert_offset,
+                         recv_rank_offset, token_row, workspace, static_cast<hipStream_t>(stream));
+}
+
+int ep_dispatch_noalloc(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                        int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                        int num_ranks, void* recv_x, int32_t* recv_src_idx,
+                        float* recv_topk_weights, int32_t* recv_expert_offset,
+                        int32_t* recv_rank_offset, int32_t* token_row, void* stream) {
+    const char* fn = "ep_dispatch_noalloc";
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (ep::dispatch_is_small(num_tokens, num_topk))
-        return hip_status(ep::launch_dispatch_small_bf16(x, topk_idx, topk_weights, num_tokens, hidden,
-                                                         num_topk, num_experts, num_ranks, 0, recv_x,
-                                                         recv_src_idx, recv_topk_weights,
-                                                         recv_expert_offset, recv_rank_offset,
-                                                         nullptr, token_row, st),
-                          fn);
-    s = hip_status(ep::launch_dispatch_index(topk_idx, topk_weights, num_tokens, num_topk,
-                                             num_experts, num_ranks, recv_src_idx,
-                                             recv_topk_weights, recv_expert_offset,
-                                             recv_rank_offset, token_row, workspace, x,
-                                             num_tokens * static_cast<int64_t>(hidden) * 2, 0,
-                                             nullptr, st),
-                   fn);
+    int s = check_dispatch_args(fn, x, topk_idx, num_tokens, hidden, num_topk, num_experts,
+                                num_ranks, recv_x, recv_src_idx, recv_expert_offset, token_row);
     if (s != EP_OK) return s;
-    return hip_status(ep::launch_dispatch_copy_bf16(x, token_row, recv_x, num_tokens * num_topk,
-                                                    num_tokens, hidden, num_topk, st),
-                      fn);
+    const size_t need = ep::index_workspace_bytes(num_tokens, num_topk, num_experts);
+    if (need > kScratchBytes)
+        return fail(EP_ERR_UNSUPPORTED,
+                    "%s: this batch needs %zu bytes of receive-order scratch; the fixed device "
+                    "array holds %zu (use ep_dispatch with a workspace)",
+                    fn, need, kScratchBytes);
+    void* ws = nullptr;
+    if (num_tokens > 0) {
+        s = scratch_for_stream(fn, st, &ws);
+        if (s != EP_OK) return s;
+    }
+    return dispatch_bf16(fn, x, topk_idx, topk_weights, num_tokens, hidden, num_topk, num_experts,
+                         num_ranks, recv_x, recv_src_idx, recv_topk_weights, recv_expert_offset,
+                         recv_rank_offset, token_row, ws, st);
 }
 
 int ep_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_weights,

@@ -51,6 +51,7 @@ def lib() -> ctypes.CDLL:
     L.ep_get_dispatch_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, sz, P]
     L.ep_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, sz, P]
     L.ep_dispatch_fp8.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, sz, P]
+    L.ep_dispatch_noalloc.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P]
     L.ep_combine.argtypes = [P, i64, P, P, i64, i32, i32, P, P]
     L.ep_dispatch_cached.argtypes = [P, P, i64, i32, i32, P, i64, P]
     L.ep_dispatch_ht_workspace_bytes.argtypes = [i64, i32]
@@ -61,7 +62,7 @@ def lib() -> ctypes.CDLL:
     L.ep_dispatch_ll_workspace_bytes.restype = sz
     L.ep_dispatch_ll.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P, sz, P]
     L.ep_dispatch_ll_fp8.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, sz, P]
-    for f in ("ep_get_dispatch_layout", "ep_dispatch", "ep_dispatch_fp8", "ep_combine",
+    for f in ("ep_get_dispatch_layout", "ep_dispatch", "ep_dispatch_noalloc", "ep_dispatch_fp8", "ep_combine",
               "ep_dispatch_cached", "ep_dispatch_fp8_cached", "ep_dispatch_ht", "ep_dispatch_ll",
               "ep_dispatch_ll_fp8"):
         getattr(L, f).restype = i32
@@ -222,6 +223,33 @@ def ep_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: Optional[
             _ptr(out["recv_expert_offset"]), _ptr(out.get("recv_rank_offset")),
             _ptr(out["token_row"]), _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "ep_dispatch")
+    return out
+
+
+def ep_dispatch_noalloc(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: Optional[torch.Tensor],
+                        num_experts: int, num_ranks: int, *,
+                        out: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
+    """ep_dispatch with the library's fixed device scratch instead of a
+    workspace: the caller passes every output (the dict ep_dispatch returns),
+    so nothing is allocated on this path."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    _need(topk_idx, "topk_idx", torch.int64, dev)
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32, dev)
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    if topk_idx.shape[0] != T:
+        raise ValueError("x and topk_idx disagree on num_tokens")
+    _check_out(out, dev, _dispatch_spec(T, k, num_experts, num_ranks, H, "recv_x",
+                                        torch.bfloat16, H, False))
+    with torch.cuda.device(dev):
+        st = lib().ep_dispatch_noalloc(
+            _ptr(x), _ptr(topk_idx), _ptr(topk_weights), T, H, k, num_experts, num_ranks,
+            _ptr(out["recv_x"]), _ptr(out["recv_src_idx"]), _ptr(out.get("recv_topk_weights")),
+            _ptr(out["recv_expert_offset"]), _ptr(out.get("recv_rank_offset")),
+            _ptr(out["token_row"]), _stream(dev))
+    _check(st, "ep_dispatch_noalloc")
     return out
 
 

@@ -149,6 +149,30 @@ int ep_dispatch(const void* x, const int64_t* topk_idx, const float* topk_weight
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * ep_dispatch_noalloc -- ep_dispatch for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same operation, kernels and outputs as ep_dispatch,
+ * with no workspace argument.  The receive-order scratch is a fixed device
+ * array inside the library, EP_NOALLOC_SCRATCH_BYTES per GPU, held until the
+ * process ends; the call itself allocates nothing.
+ *
+ * Arguments and outputs as ep_dispatch.  The stream must belong to the
+ * current HIP device.  A batch whose scratch need,
+ * ep_dispatch_workspace_bytes(T, k, E), exceeds EP_NOALLOC_SCRATCH_BYTES
+ * returns EP_ERR_UNSUPPORTED before anything is enqueued (e.g. 32768 tokens
+ * at top-8 need 64 KiB + 256 B over 256 experts, 512 KiB + 256 B over 2048).
+ * All calls on one GPU share that GPU's array: calls that overlap on one GPU
+ * (two streams, two threads) race and must be serialised by the caller.
+ * ------------------------------------------------------------------------- */
+#define EP_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+int ep_dispatch_noalloc(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                        int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                        int num_ranks, void* recv_x, int32_t* recv_src_idx,
+                        float* recv_topk_weights, int32_t* recv_expert_offset,
+                        int32_t* recv_rank_offset, int32_t* token_row, void* stream);
+
+/* ---------------------------------------------------------------------------
  * ep_dispatch_fp8 -- ep_dispatch with the low-latency FP8 cast (low-latency
  * port commit, dispatch<kUseFP8,...>).  For token t and 128-channel block c:
  *   a = max |x[t, 128c .. 128c+127]|,  s = a / 448 (IEEE fp32 division),

@@ -259,3 +259,26 @@ def test_c_caller_compiles_and_links(tmp_path):
     ep.lib()                                   # libep.so is built
     mod.EXE = str(tmp_path / "ep_c_caller")
     assert os.path.exists(mod.build())
+
+
+def test_dispatch_noalloc_host_rejects():
+    """The no-allocation dispatch validates like ep_dispatch, and refuses a
+    batch whose receive-order scratch need exceeds its fixed device array,
+    all before any HIP call."""
+    L = ep.lib()
+
+    def call(**kw):
+        a = dict(x=FAKE, idx=FAKE, w=None, T=16, H=256, k=2, E=8, R=4, recv=FAKE, src=FAKE,
+                 rw=None, eoff=FAKE, roff=None, trow=FAKE)
+        a.update(kw)
+        return L.ep_dispatch_noalloc(a["x"], a["idx"], a["w"], a["T"], a["H"], a["k"], a["E"], a["R"],
+                                     a["recv"], a["src"], a["rw"], a["eoff"], a["roff"], a["trow"], None)
+
+    for kw in (dict(H=12), dict(x=None), dict(trow=None), dict(eoff=None), dict(E=9),
+               dict(recv=ctypes.c_void_p(0x100004))):
+        assert call(**kw) == EINVAL, kw
+    assert call(k=100) == EUNSUP
+    big = dict(T=8192, k=64, E=2048, R=64, H=8)
+    assert ep.ep_dispatch_workspace_bytes(8192, 64, 2048) > (1 << 20)
+    assert call(**big) == EUNSUP
+    assert b"scratch" in L.ep_last_error()
