@@ -24,14 +24,18 @@ The headline `value` is
 
     (algorithmic bytes of ep_dispatch + ep_combine) / (t_dispatch + t_combine)
 
-in GB/s, summed over the timed steps.  Secondary figures: `full_path` adds
-the layout call, and `payload_convention` counts bytes as the pages' own
-benchmark does (one bf16 row per dispatched (token, expert) pair in each
-direction, over the same times).  `roofline` reports the combine kernel
-(one kernel per ep_combine call) against the 8 TB/s HBM3E peak; `traffic`
-comes from committed rocprofv3 FETCH_SIZE / WRITE_SIZE counters when they
-were taken on the current kernel source, else null.  `cpu_baseline` times
-the C oracle (single thread) on the same workload on this host.
+in GB/s, summed over the timed steps, and `ms_per_step` is that
+t_dispatch + t_combine per step; the layout and FP8 dispatch of each step are
+timed as phases of their own.  Secondary figures: `full_path` adds the layout
+call, and `payload_convention` counts bytes as the pages' own benchmark does
+(one bf16 row per dispatched (token, expert) pair in each direction, over the
+same times).  `roofline` reports the combine kernel (one kernel per
+ep_combine call) against the 8 TB/s HBM3E peak; `traffic` comes from
+committed rocprofv3 FETCH_SIZE / WRITE_SIZE counters when they were taken on
+the current kernel source, else null.  `cpu_baseline` times the C oracle
+(single thread) on the same workload on this host.  `per_config` then repeats
+the measurement (fewer steps) on each of the five workloads -- tiny, dsv3,
+skewed, ll_fp8, large -- each with its own oracle timing on this host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3]
 """
@@ -205,6 +209,13 @@ def cpu_baseline(wl, x, idx, w, budget_s):
     }
 
 
+def oracle_entry(cpu):
+    """The per-workload part of a cpu_baseline record."""
+    return {"GBps": cpu["value"], "cores": cpu["cores"], "dispatch_ms": cpu["dispatch_ms"],
+            "combine_ms": cpu["combine_ms"], "layout_ms": cpu["layout_ms"],
+            "dispatch_fp8_us_per_token": cpu["dispatch_fp8_us_per_token"], "sample": cpu["sample"]}
+
+
 def graph_mode(args, wl, ep, torch, np, idxd, xd, wd, lay, ws_l, disp, ws_d, comb, fp8):
     """Eager vs HIP-graph replay of one whole step, caches left warm."""
     E, R, P, N = wl.E, wl.R, wl.P, wl.T * wl.k
@@ -288,48 +299,22 @@ def drain_check(args, wl, ep, torch, np, idxd, xd, wd, disp, ws_d, comb, flush):
     print(json.dumps(res), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="dsv3")
-    ap.add_argument("--no-flush", action="store_true", help="do not evict caches between phases")
-    ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
-    ap.add_argument("--skip-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true",
-                    help="instead of the headline: time one whole step (layout, dispatch, combine, "
-                         "FP8 dispatch; no cache eviction) replayed from a captured HIP graph "
-                         "against the same step launched eagerly")
-    ap.add_argument("--drain-check", action="store_true",
-                    help="instead of the headline: check that ep_dispatch and ep_combine leave no "
-                         "write-backs behind their end events (each timed alone and followed by "
-                         "a 512 MiB read)")
-    ap.add_argument("--ll-capacity", type=int, default=0,
-                    help="capacity (rows per expert) of the padded-layout phases; default: the "
-                         "busiest expert's load rounded up to 64 rows")
-    ap.add_argument("--calibration-copy", action="store_true",
-                    help="after the timed steps, run 4 plain 256 MiB device copies (a known-size "
-                         "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
-    args = ap.parse_args()
+# Steps of the per-workload measurements that follow the headline (latency-
+# bound batches take more steps: each costs a few microseconds).
+PER_CONFIG_STEPS = {"tiny": 200, "ll_fp8": 200}
+PER_CONFIG_DEFAULT_STEPS = 20
+PER_CONFIG_WARMUP = 5
+PER_CONFIG_CPU_SECONDS = 2.0
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
-              "every destination rank is a partition of one GPU's HBM here; run with --gpus 1.",
-              file=sys.stderr)
-        sys.exit(2)
 
-    import numpy as np
-    import torch
+def measure(wl, steps, warmup, args, ep, torch, np, mode=None):
+    """Time every phase of `steps` steps of workload wl (after `warmup`
+    untimed steps).  Returns the phase times (ms arrays), algorithmic bytes
+    and derived figures; with mode = "graph" / "drain" it runs that
+    measurement instead and returns None."""
+    from combine_get_dispatch_02_amd.workloads import make_workload
 
-    from combine_get_dispatch_02_amd import ep
-    from combine_get_dispatch_02_amd.workloads import CONFIGS, make_workload
-
-    wl = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    log(f"[bench] {wl.describe()} steps={args.steps} warmup={args.warmup} ({ep.version()})")
     x, idx, w = make_workload(wl)
     xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
     idxd = torch.from_numpy(idx).to(dev)
@@ -357,6 +342,7 @@ def main():
     fp8["recv_scales"] = torch.empty((N, H // 128), dtype=torch.float32, device=dev)
     ws_d = torch.empty(ep.ep_dispatch_workspace_bytes(T, k, E), dtype=torch.uint8, device=dev)
     comb = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    n_ht = ht_rows(wl, idx)
     cap_ht = T * R
     ht = dict(recv_x=torch.empty((cap_ht, H), dtype=torch.bfloat16, device=dev),
               recv_src_idx=torch.empty(cap_ht, dtype=torch.int32, device=dev),
@@ -366,7 +352,6 @@ def main():
               token_rank_row=torch.empty((T, R), dtype=torch.int32, device=dev))
     ws_ht = torch.empty(ep.ep_dispatch_ht_workspace_bytes(T, R), dtype=torch.uint8, device=dev)
     comb_ht = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    n_ht = ht_rows(wl, idx)
     cap_ll = args.ll_capacity or ll_capacity(wl, idx)
     n_ll = int(np.minimum(np.bincount(idx[(idx >= 0) & (idx < E)], minlength=E), cap_ll).sum())
     ll = dict(recv_x=torch.empty((E, cap_ll, H), dtype=torch.bfloat16, device=dev),
@@ -388,69 +373,48 @@ def main():
     flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     flush_src = torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
 
-    phases = ["layout", "dispatch", "combine", "dispatch_fp8", "dispatch_ht", "combine_ht",
-              "dispatch_ll", "combine_ll", "dispatch_ll_fp8", "dispatch_cached", "dispatch_fp8_cached"]
-
     def flush(i):
         if not args.no_flush:
             flush_buf.fill_(i & 0xFF)
             flush_src.sum()
 
+    calls = [
+        ("layout", lambda: ep.ep_get_dispatch_layout(idxd, E, R, P, out=lay, workspace=ws_l)),
+        ("dispatch", lambda: ep.ep_dispatch(xd, idxd, wd, E, R, out=disp, workspace=ws_d)),
+        ("combine", lambda: ep.ep_combine(disp["recv_x"], disp["token_row"], wd, num_rows=N, out=comb)),
+        ("dispatch_fp8", lambda: ep.ep_dispatch_fp8(xd, idxd, wd, E, R, out=fp8, workspace=ws_d)),
+        ("dispatch_ht", lambda: ep.ep_dispatch_ht(xd, idxd, wd, E, R, out=ht, workspace=ws_ht)),
+        ("combine_ht", lambda: ep.ep_combine(ht["recv_x"], ht["token_rank_row"], None, num_rows=n_ht,
+                                             out=comb_ht)),
+        ("dispatch_ll", lambda: ep.ep_dispatch_ll(xd, idxd, wd, E, cap_ll, out=ll, workspace=ws_ll)),
+        ("combine_ll", lambda: ep.ep_combine(ll["recv_x"].view(E * cap_ll, H), ll["token_slot"], wd,
+                                             out=comb_ll)),
+        ("dispatch_ll_fp8", lambda: ep.ep_dispatch_ll_fp8(xd, idxd, wd, E, cap_ll, out=ll8,
+                                                          workspace=ws_ll)),
+        ("dispatch_cached", lambda: ep.ep_dispatch_cached(xd, disp["token_row"], N, out=cached)),
+        ("dispatch_fp8_cached", lambda: ep.ep_dispatch_fp8_cached(xd, fp8["token_row"], N, out=cached8)),
+    ]
+    phases = [name for name, _ in calls]
+
+    if mode == "graph":
+        graph_mode(args, wl, ep, torch, np, idxd, xd, wd, lay, ws_l, disp, ws_d, comb, fp8)
+        return None
+    if mode == "drain":
+        drain_check(args, wl, ep, torch, np, idxd, xd, wd, disp, ws_d, comb, flush)
+        return None
+
     def step(i, ev):
-        flush(i)
-        ev[0].record()
-        ep.ep_get_dispatch_layout(idxd, E, R, P, out=lay, workspace=ws_l)
-        ev[1].record()
-        ep.ep_dispatch(xd, idxd, wd, E, R, out=disp, workspace=ws_d)
-        ev[2].record()
-        flush(i + 1)
-        ev[3].record()
-        ep.ep_combine(disp["recv_x"], disp["token_row"], wd, num_rows=N, out=comb)
-        ev[4].record()
-        flush(i + 2)
-        ev[5].record()
-        ep.ep_dispatch_fp8(xd, idxd, wd, E, R, out=fp8, workspace=ws_d)
-        ev[6].record()
-        flush(i + 3)
-        ev[7].record()
-        ep.ep_dispatch_ht(xd, idxd, wd, E, R, out=ht, workspace=ws_ht)
-        ev[8].record()
-        flush(i + 4)
-        ev[9].record()
-        ep.ep_combine(ht["recv_x"], ht["token_rank_row"], None, num_rows=n_ht, out=comb_ht)
-        ev[10].record()
-        flush(i + 5)
-        ev[11].record()
-        ep.ep_dispatch_ll(xd, idxd, wd, E, cap_ll, out=ll, workspace=ws_ll)
-        ev[12].record()
-        flush(i + 6)
-        ev[13].record()
-        ep.ep_combine(ll["recv_x"].view(E * cap_ll, H), ll["token_slot"], wd, out=comb_ll)
-        ev[14].record()
-        flush(i + 7)
-        ev[15].record()
-        ep.ep_dispatch_ll_fp8(xd, idxd, wd, E, cap_ll, out=ll8, workspace=ws_ll)
-        ev[16].record()
-        flush(i + 8)
-        ev[17].record()
-        ep.ep_dispatch_cached(xd, disp["token_row"], N, out=cached)
-        ev[18].record()
-        flush(i + 9)
-        ev[19].record()
-        ep.ep_dispatch_fp8_cached(xd, fp8["token_row"], N, out=cached8)
-        ev[20].record()
+        # every phase starts from evicted caches; its events bracket only its call
+        for p_i, (_, fn) in enumerate(calls):
+            flush(i + p_i)
+            ev[2 * p_i].record()
+            fn()
+            ev[2 * p_i + 1].record()
 
     def events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(21)]
+        return [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(calls))]
 
-    if args.graph:
-        graph_mode(args, wl, ep, torch, np, idxd, xd, wd, lay, ws_l, disp, ws_d, comb, fp8)
-        return
-    if args.drain_check:
-        drain_check(args, wl, ep, torch, np, idxd, xd, wd, disp, ws_d, comb, flush)
-        return
-
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i, events())
     torch.cuda.synchronize()
     if disp["recv_expert_offset"][-1].item() != N:
@@ -460,73 +424,156 @@ def main():
     if ll["recv_count"].sum().item() != n_ll or ll8["recv_count"].sum().item() != n_ll:
         raise RuntimeError("padded dispatch filled an unexpected number of slots")
 
-    evs = [events() for _ in range(args.steps)]
+    evs = [events() for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms = {p: np.array([e[2 * i].elapsed_time(e[2 * i + 1]) for e in evs]) for i, p in enumerate(phases)}
 
-    # Secondary: the same dispatch and combine with warm caches (no eviction).
-    warm_ev = []
-    for i in range(max(args.steps // 5, 5)):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        e[0].record()
-        ep.ep_dispatch(xd, idxd, wd, E, R, out=disp, workspace=ws_d)
-        e[1].record()
-        ep.ep_combine(disp["recv_x"], disp["token_row"], wd, num_rows=N, out=comb)
-        e[2].record()
-        warm_ev.append(e)
-    torch.cuda.synchronize()
-    warm_d = np.array([e[0].elapsed_time(e[1]) for e in warm_ev[1:]]) * 1e3
-    warm_c = np.array([e[1].elapsed_time(e[2]) for e in warm_ev[1:]]) * 1e3
-
-    if args.calibration_copy:
-        cal_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
-        cal_dst = torch.empty_like(cal_src)
+    res = dict(wl=wl, x=x, idx=idx, w=w, ms=ms, wall=wall, steps=steps, n_ht=n_ht, cap_ll=cap_ll,
+               n_ll=n_ll, B=algorithmic_bytes(wl, n_ht, n_ll), phases=phases)
+    if mode == "headline":
+        # Secondary: the same dispatch and combine with warm caches (no eviction).
+        warm_ev = []
+        for i in range(max(steps // 5, 5)):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            calls[1][1]()
+            e[1].record()
+            calls[2][1]()
+            e[2].record()
+            warm_ev.append(e)
         torch.cuda.synchronize()
-        for _ in range(4):
-            cal_dst.copy_(cal_src)
-        torch.cuda.synchronize()
+        res["warm_d"] = np.array([e[0].elapsed_time(e[1]) for e in warm_ev[1:]]) * 1e3
+        res["warm_c"] = np.array([e[1].elapsed_time(e[2]) for e in warm_ev[1:]]) * 1e3
+        if args.calibration_copy:
+            cal_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+            cal_dst = torch.empty_like(cal_src)
+            torch.cuda.synchronize()
+            for _ in range(4):
+                cal_dst.copy_(cal_src)
+            torch.cuda.synchronize()
+        # An event pair with nothing between it, after the same eviction: the
+        # part of every phase time that is the events' own cost, not the kernel's.
+        empty = []
+        for i in range(20):
+            flush(i)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            b.record()
+            torch.cuda.synchronize()
+            empty.append(a.elapsed_time(b) * 1e3)
+        res["pair_us"] = float(np.median(empty))
+    return res
 
-    ms = {p: np.array([e[a].elapsed_time(e[b]) for e in evs])
-          for p, (a, b) in zip(phases, [(0, 1), (1, 2), (3, 4), (5, 6), (7, 8), (9, 10), (11, 12),
-                                        (13, 14), (15, 16), (17, 18), (19, 20)])}
-    B = algorithmic_bytes(wl, n_ht, n_ll)
+
+def phase_summary(res, np):
+    """Per phase: mean / median / p10 / p90 event time, algorithmic bytes,
+    GB/s and fraction of the HBM peak."""
+    out = {}
+    for p in res["phases"]:
+        us = res["ms"][p] * 1e3
+        gbs = res["B"][p] / (us.mean() * 1e-6) / 1e9
+        out[p] = {"us_mean": round(float(us.mean()), 2), "us_median": round(float(np.median(us)), 2),
+                  "us_p10": round(float(np.percentile(us, 10)), 2),
+                  "us_p90": round(float(np.percentile(us, 90)), 2),
+                  "alg_bytes": int(res["B"][p]), "GBps": round(gbs, 1),
+                  "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
+
+
+def pair_gbs(res, a, b):
+    """Algorithmic bytes of phases a + b over their summed event times (GB/s)."""
+    t = float(res["ms"][a].sum() + res["ms"][b].sum()) / 1e3
+    return (res["B"][a] + res["B"][b]) * res["steps"] / t / 1e9
+
+
+def config_entry(res, np, cpu):
+    """Compact per-workload record of the bench line."""
+    ms = res["ms"]
+    wl = res["wl"]
+    v = pair_gbs(res, "dispatch", "combine")
+    us = lambda p: round(float(ms[p].mean()) * 1e3, 2)  # noqa: E731
+    frac = lambda p: round(res["B"][p] / (ms[p].mean() * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)  # noqa: E731
+    e = {"workload": wl.describe(), "steps": res["steps"],
+         "dispatch_plus_combine_GBps": round(v, 1), "frac_of_hbm_peak": round(v / HBM_PEAK_GBS, 4),
+         "dispatch_us": us("dispatch"), "dispatch_frac": frac("dispatch"),
+         "combine_us": us("combine"), "combine_frac": frac("combine"),
+         "dispatch_fp8_us": us("dispatch_fp8"), "dispatch_fp8_frac": frac("dispatch_fp8"),
+         "layout_us": us("layout"),
+         "ht_pair_frac": round(pair_gbs(res, "dispatch_ht", "combine_ht") / HBM_PEAK_GBS, 4),
+         "ll_pair_frac": round(pair_gbs(res, "dispatch_ll", "combine_ll") / HBM_PEAK_GBS, 4),
+         "dispatch_copy_frac": frac("dispatch_cached"), "fp8_copy_frac": frac("dispatch_fp8_cached"),
+         "oracle": cpu}
+    if wl.T * wl.H * 2 < (64 << 20):
+        e["note"] = ("latency-bound: the whole path fits the 256 MB Infinity Cache and each call "
+                     "lasts a few launch latencies, so the HBM fraction is not a roofline here")
+    return e
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict caches between phases")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-per-config", action="store_true",
+                    help="time the headline workload only (no per_config records)")
+    ap.add_argument("--graph", action="store_true",
+                    help="instead of the headline: time one whole step (layout, dispatch, combine, "
+                         "FP8 dispatch; no cache eviction) replayed from a captured HIP graph "
+                         "against the same step launched eagerly")
+    ap.add_argument("--drain-check", action="store_true",
+                    help="instead of the headline: check that ep_dispatch and ep_combine leave no "
+                         "write-backs behind their end events (each timed alone and followed by "
+                         "a 512 MiB read)")
+    ap.add_argument("--ll-capacity", type=int, default=0,
+                    help="capacity (rows per expert) of the padded-layout phases; default: the "
+                         "busiest expert's load rounded up to 64 rows")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="after the timed steps, run 4 plain 256 MiB device copies (a known-size "
+                         "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "every destination rank is a partition of one GPU's HBM here; run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from combine_get_dispatch_02_amd import ep
+    from combine_get_dispatch_02_amd.workloads import CONFIGS
+
+    wl = CONFIGS[args.workload]
+    torch.cuda.set_device(torch.device("cuda:0"))
+    log(f"[bench] {wl.describe()} steps={args.steps} warmup={args.warmup} ({ep.version()})")
+    if args.graph or args.drain_check:
+        measure(wl, args.steps, args.warmup, args, ep, torch, np,
+                mode="graph" if args.graph else "drain")
+        return
+
+    res = measure(wl, args.steps, args.warmup, args, ep, torch, np, mode="headline")
+    ms, B, N, H = res["ms"], res["B"], wl.T * wl.k, wl.H
+    T, k, E, R, P = wl.T, wl.k, wl.E, wl.R, wl.P
     t_dc = float(ms["dispatch"].sum() + ms["combine"].sum()) / 1e3
     value = (B["dispatch"] + B["combine"]) * args.steps / t_dc / 1e9
-    step_ms = float(sum(ms[p].mean() for p in phases[:4]))
-    t_ht = float(ms["dispatch_ht"].sum() + ms["combine_ht"].sum()) / 1e3
-    ht_gbs = (B["dispatch_ht"] + B["combine_ht"]) * args.steps / t_ht / 1e9
-    t_ll = float(ms["dispatch_ll"].sum() + ms["combine_ll"].sum()) / 1e3
-    ll_gbs = (B["dispatch_ll"] + B["combine_ll"]) * args.steps / t_ll / 1e9
-    phase_info = {}
-    for p in phases:
-        us = ms[p] * 1e3
-        gbs = B[p] / (us.mean() * 1e-6) / 1e9
-        phase_info[p] = {"us_mean": round(float(us.mean()), 2), "us_median": round(float(np.median(us)), 2),
-                         "us_p10": round(float(np.percentile(us, 10)), 2),
-                         "us_p90": round(float(np.percentile(us, 90)), 2),
-                         "alg_bytes": int(B[p]), "GBps": round(gbs, 1),
-                         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    phase_info = phase_summary(res, np)
     full_us = float(sum(ms[p].mean() for p in ("layout", "dispatch", "combine"))) * 1e3
     full_b = B["layout"] + B["dispatch"] + B["combine"]
     payload_b = 2 * 2 * N * H
     c_us = float(ms["combine"].mean()) * 1e3
     achieved = B["combine"] / (c_us * 1e-6) / 1e9
     traffic = load_traffic(B["combine"])
-    # An event pair with nothing between it, after the same eviction: the part
-    # of every phase time that is the events' own cost, not the kernel's.
-    empty = []
-    for i in range(20):
-        flush(i)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        b.record()
-        torch.cuda.synchronize()
-        empty.append(a.elapsed_time(b) * 1e3)
-    pair_us = float(np.median(empty))
     k_us = float(ms["dispatch_cached"].mean()) * 1e3
     k_gbs = B["dispatch_cached"] / (k_us * 1e-6) / 1e9
     roofline_copy = {"kernel": "copy_bf16_kernel (ep_dispatch_cached: the dispatch copy alone, "
@@ -543,14 +590,31 @@ def main():
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "alg_bytes_per_launch": int(B["combine"]), "avg_launch_us": round(c_us, 2),
-                "empty_event_pair_us": round(pair_us, 2),
+                "empty_event_pair_us": round(res["pair_us"], 2),
                 "note": "avg_launch_us is the HIP-event time of the one-kernel ep_combine call, so it "
                         "includes one event pair; the kernel-trace average is lower by about that"}
 
     cpu = None
     if not args.skip_cpu_baseline:
         log(f"[bench] cpu baseline (oracle, ~{args.cpu_baseline_seconds:.0f} s)")
-        cpu = cpu_baseline(wl, x, idx, w, args.cpu_baseline_seconds)
+        cpu = cpu_baseline(wl, res["x"], res["idx"], res["w"], args.cpu_baseline_seconds)
+
+    per_config = {}
+    if not args.skip_per_config:
+        for name, other in CONFIGS.items():
+            if name == wl.name:
+                per_config[name] = config_entry(res, np, cpu and oracle_entry(cpu))
+                continue
+            st = PER_CONFIG_STEPS.get(name, PER_CONFIG_DEFAULT_STEPS)
+            log(f"[bench] per-config {other.describe()} steps={st}")
+            r = measure(other, st, PER_CONFIG_WARMUP, args, ep, torch, np)
+            torch.cuda.empty_cache()
+            c = None
+            if not args.skip_cpu_baseline:
+                c = oracle_entry(cpu_baseline(other, r["x"], r["idx"], r["w"], PER_CONFIG_CPU_SECONDS))
+            per_config[name] = config_entry(r, np, c)
+            del r
+            torch.cuda.empty_cache()
 
     line = {
         "metric": METRIC,
@@ -559,7 +623,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 4),
+        "ms_per_step": round(1e3 * t_dc / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -568,25 +632,29 @@ def main():
         "config": {"workload": wl.describe(), "T": T, "H": H, "k": k, "num_experts": E,
                    "num_ranks": R, "ranks_per_group": P, "global_batch": T, "parallelism": "none (1 GPU)"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "ms_per_step_note": "ep_dispatch + ep_combine, the time value is computed from; the layout "
+                            "and FP8 dispatch of each step are timed separately (phases)",
+        "layout_ms_per_step": round(float(ms["layout"].mean()), 4),
+        "dispatch_fp8_ms_per_step": round(float(ms["dispatch_fp8"].mean()), 4),
         "caches_flushed_between_phases": not args.no_flush,
-        "wall_ms_per_step_incl_flush": round(1e3 * wall / args.steps, 4),
+        "wall_ms_per_step_incl_flush": round(1e3 * res["wall"] / args.steps, 4),
         "phases": phase_info,
-        "warm": {"dispatch_us": round(float(np.median(warm_d)), 2),
-                 "combine_us": round(float(np.median(warm_c)), 2),
+        "warm": {"dispatch_us": round(float(np.median(res["warm_d"])), 2),
+                 "combine_us": round(float(np.median(res["warm_c"])), 2),
                  "value": round((B["dispatch"] + B["combine"]) /
-                                ((np.median(warm_d) + np.median(warm_c)) * 1e-6) / 1e9, 1),
+                                ((np.median(res["warm_d"]) + np.median(res["warm_c"])) * 1e-6) / 1e9, 1),
                  "note": "secondary: dispatch then combine back to back, no cache eviction "
                          "(x and part of the rows may be served from the 256 MB Infinity Cache)"},
-        "rank_dedup": {"rows": n_ht, "rows_per_token": round(n_ht / max(T, 1), 4),
-                       "dispatch_plus_combine_GBps": round(ht_gbs, 1),
-                       "pct_of_hbm_peak": round(100 * ht_gbs / HBM_PEAK_GBS, 2),
-                       "us_per_pair": round(1e6 * t_ht / args.steps, 2),
+        "rank_dedup": {"rows": res["n_ht"], "rows_per_token": round(res["n_ht"] / max(T, 1), 4),
+                       "dispatch_plus_combine_GBps": round(pair_gbs(res, "dispatch_ht", "combine_ht"), 1),
+                       "pct_of_hbm_peak": round(100 * pair_gbs(res, "dispatch_ht", "combine_ht") / HBM_PEAK_GBS, 2),
+                       "us_per_pair": round(1e3 * float(ms["dispatch_ht"].mean() + ms["combine_ht"].mean()), 2),
                        "note": "ep_dispatch_ht + unweighted ep_combine; not part of value or ms_per_step"},
-        "ll_padded": {"capacity": cap_ll, "slots_filled": n_ll, "slots_dropped": N - n_ll,
-                      "slots_allocated": E * cap_ll,
-                      "dispatch_plus_combine_GBps": round(ll_gbs, 1),
-                      "pct_of_hbm_peak": round(100 * ll_gbs / HBM_PEAK_GBS, 2),
-                      "us_per_pair": round(1e6 * t_ll / args.steps, 2),
+        "ll_padded": {"capacity": res["cap_ll"], "slots_filled": res["n_ll"], "slots_dropped": N - res["n_ll"],
+                      "slots_allocated": E * res["cap_ll"],
+                      "dispatch_plus_combine_GBps": round(pair_gbs(res, "dispatch_ll", "combine_ll"), 1),
+                      "pct_of_hbm_peak": round(100 * pair_gbs(res, "dispatch_ll", "combine_ll") / HBM_PEAK_GBS, 2),
+                      "us_per_pair": round(1e3 * float(ms["dispatch_ll"].mean() + ms["combine_ll"].mean()), 2),
                       "note": "ep_dispatch_ll + ep_combine over token_slot, capacity = busiest "
                               "expert's load rounded up to 64 rows (nothing dropped); not part of "
                               "value or ms_per_step"},
@@ -604,6 +672,7 @@ def main():
         "roofline_dispatch_copy": roofline_copy,
         "roofline_fp8_copy": roofline_fp8,
         "cpu_baseline": cpu,
+        "per_config": per_config,
     }
     print(json.dumps(line), flush=True)
 
