@@ -332,22 +332,19 @@ def drain_check(args, wl, ep, torch, np, idxd, xd, wd, disp, ws_d, comb, flush):
 
 
 def scatter_check(args, wl, ep, torch, np, xd, disp, fp8, cached, cached8, flush):
-    """The copy kernels alone (ep_dispatch_cached / ep_dispatch_fp8_cached) on
-    the real receive map and on an identity map that sends token t's slots to
-    rows t*k .. t*k+k-1: the same bytes, but one sequential write stream
-    instead of one per expert.  Each with x evicted (read from HBM) and with
-    x read once through the caches just before the call."""
+    """The copy kernels alone (ep_dispatch_cached / ep_dispatch_fp8_cached),
+    caches evicted before each call, on the real receive map and on an
+    identity map that sends token t's slots to rows t*k .. t*k+k-1: the same
+    bytes read and written, but one sequential write stream instead of one
+    per expert."""
     T, k = wl.T, wl.k
     N = T * k
     ident = torch.arange(N, dtype=torch.int32, device=xd.device).view(T, k)
-    xsum = torch.empty((), dtype=torch.int64, device=xd.device)
 
-    def timed(fn, warm):
+    def timed(fn):
         ts = []
         for i in range(args.warmup + args.steps):
             flush(i)
-            if warm:
-                torch.sum(xd.view(torch.int16), dtype=torch.int64, out=xsum)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             fn()
@@ -361,8 +358,7 @@ def scatter_check(args, wl, ep, torch, np, xd, disp, fp8, cached, cached8, flush
     for name, fn in (("bf16", lambda m: ep.ep_dispatch_cached(xd, m, N, out=cached)),
                      ("fp8", lambda m: ep.ep_dispatch_fp8_cached(xd, m, N, out=cached8))):
         for mname, m in (("real_map", disp["token_row"]), ("identity_map", ident)):
-            for warm in (False, True):
-                res[f"{name}_{mname}_{'x_cached' if warm else 'x_in_hbm'}_us"] = timed(lambda: fn(m), warm)
+            res[f"{name}_{mname}_us"] = timed(lambda: fn(m))
     print(json.dumps(res), flush=True)
 
 
@@ -607,8 +603,7 @@ def main():
                          "a 512 MiB read)")
     ap.add_argument("--scatter-check", action="store_true",
                     help="instead of the headline: time the dispatch copy kernels alone on the real "
-                         "receive map and on an identity map (one sequential write stream), x in HBM "
-                         "and x cached")
+                         "receive map and on an identity map (one sequential write stream)")
     ap.add_argument("--ll-capacity", type=int, default=0,
                     help="capacity (rows per expert) of the padded-layout phases; default: the "
                          "busiest expert's load rounded up to 64 rows")
