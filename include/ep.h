@@ -20,7 +20,8 @@
  * ----------------------------------------
  * Pointers.  Every array argument is a DEVICE pointer (HBM of the current HIP
  * device), row-major and densely packed, owned by the caller; the library
- * keeps no reference after the call returns and allocates nothing.  The
+ * keeps no reference after the call returns and allocates nothing at run
+ * time (ep_dispatch_noalloc's fixed scratch is part of the loaded code).  The
  * workspace is caller-owned device memory of at least the size reported by
  * the matching *_workspace_bytes() call, 4-byte aligned (the kernels keep
  * 32-bit counters there; EP_ERR_INVALID_ARGUMENT otherwise); its contents on
@@ -32,7 +33,9 @@
  * only validates its arguments on the host and enqueues kernels on `stream`;
  * it never synchronises.  Outputs are valid once the stream reaches that
  * point.  Calls on different streams touching disjoint buffers may run
- * concurrently; the library holds no mutable global state.
+ * concurrently; the library holds no mutable global state apart from the
+ * fixed device scratch of ep_dispatch_noalloc (below) and the per-device
+ * cache of its address, filled once under a lock.
  *
  * Routing slots.  Slot (t, j) is valid iff 0 <= topk_idx[t*k + j] <
  * num_experts.  Any other value (conventionally -1) is an empty slot: it gets
