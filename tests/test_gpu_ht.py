@@ -5,7 +5,6 @@ implementation #852", PR body "Scope / Intranode").
 Bar: every map and every dispatched byte bit-exact; combine within the 8e-3
 relative bound and, because both sides sum in rank order in fp32, bit-exact.
 """
-import dataclasses
 
 import numpy as np
 import pytest

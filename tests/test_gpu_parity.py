@@ -25,7 +25,7 @@ import oracle
 from combine_get_dispatch_02_amd import ep
 from combine_get_dispatch_02_amd.workloads import (CONFIGS, expert_outputs, make_workload, mask_slots,
                                                    pooled_expert_outputs, random_bf16)
-from parity import assert_combine, assert_fp8_codes, f32  # noqa: F401  (f32 re-exported)
+from parity import assert_combine, assert_fp8_codes
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
