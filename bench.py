@@ -364,8 +364,8 @@ def scatter_check(args, wl, ep, torch, np, xd, disp, fp8, cached, cached8, flush
 
 # Steps of the per-workload measurements that follow the headline (latency-
 # bound batches take more steps: each costs a few microseconds).
-PER_CONFIG_STEPS = {"tiny": 200, "ll_fp8": 200}
-PER_CONFIG_DEFAULT_STEPS = 20
+PER_CONFIG_STEPS = {"tiny": 1000, "ll_fp8": 1000}
+PER_CONFIG_DEFAULT_STEPS = 100
 PER_CONFIG_WARMUP = 5
 PER_CONFIG_CPU_SECONDS = 2.0
 
@@ -565,6 +565,9 @@ def config_entry(res, np, cpu):
     wl = res["wl"]
     v = pair_gbs(res, "dispatch", "combine")
     us = lambda p: round(float(ms[p].mean()) * 1e3, 2)  # noqa: E731
+    pct = lambda p: {"median": round(float(np.median(ms[p])) * 1e3, 2),  # noqa: E731
+                     "p10": round(float(np.percentile(ms[p], 10)) * 1e3, 2),
+                     "p90": round(float(np.percentile(ms[p], 90)) * 1e3, 2)}
     frac = lambda p: round(res["B"][p] / (ms[p].mean() * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)  # noqa: E731
     e = {"workload": wl.describe(), "steps": res["steps"],
          "dispatch_plus_combine_GBps": round(v, 1), "frac_of_hbm_peak": round(v / HBM_PEAK_GBS, 4),
@@ -572,6 +575,7 @@ def config_entry(res, np, cpu):
          "combine_us": us("combine"), "combine_frac": frac("combine"),
          "dispatch_fp8_us": us("dispatch_fp8"), "dispatch_fp8_frac": frac("dispatch_fp8"),
          "layout_us": us("layout"),
+         "us_percentiles": {p: pct(p) for p in ("dispatch", "combine", "dispatch_fp8")},
          "ht_pair_frac": round(pair_gbs(res, "dispatch_ht", "combine_ht") / HBM_PEAK_GBS, 4),
          "ll_pair_frac": round(pair_gbs(res, "dispatch_ll", "combine_ll") / HBM_PEAK_GBS, 4),
          "dispatch_copy_frac": frac("dispatch_cached"), "fp8_copy_frac": frac("dispatch_fp8_cached"),
