@@ -49,33 +49,30 @@ constexpr int kHtTile = 256;          // tokens per tile = threads per block
 constexpr int kHtWaves = kHtTile / kWave;
 constexpr int kHtHistBatch = 64;
 
-// Rank of a valid expert id (0 <= e < E <= 2048): a 32-bit division (a 64-bit
-// one is a long software sequence on this target).
-__device__ __forceinline__ int rank_of(int64_t e, int epr) {
-    return static_cast<int>(static_cast<uint32_t>(e) / static_cast<uint32_t>(epr));
-}
-
-__device__ __forceinline__ uint64_t rank_mask(const int64_t* __restrict__ ids, int k, int E, int epr) {
+// Ranks of valid expert ids: rank_of (ep_ids.h), a multiply-high by
+// magic = rank_magic(E / R).
+__device__ __forceinline__ uint64_t rank_mask(const int64_t* __restrict__ ids, int k, int E, uint32_t magic) {
     uint64_t m = 0;
     for (int j0 = 0; j0 < k; j0 += kIdBatch) {
         int64_t v[kIdBatch];
         load_ids(ids, j0, k, v);
 #pragma unroll
         for (int u = 0; u < kIdBatch; ++u)
-            if (v[u] >= 0 && v[u] < E) m |= uint64_t(1) << rank_of(v[u], epr);
+            if (v[u] >= 0 && v[u] < E) m |= uint64_t(1) << rank_of(v[u], magic);
     }
     return m;
 }
 
 __global__ __launch_bounds__(kHtTile) void ht_tile_hist_kernel(const int64_t* __restrict__ topk_idx,
                                                               int64_t T, int k, int E, int R,
+                                                              uint32_t magic,
                                                               int32_t* __restrict__ hist) {
     __shared__ int32_t h[EP_MAX_RANKS];
     if (threadIdx.x < R) h[threadIdx.x] = 0;
     __syncthreads();
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kHtTile + threadIdx.x;
     if (t < T) {
-        for (uint64_t b = rank_mask(topk_idx + t * k, k, E, E / R); b; b &= b - 1)
+        for (uint64_t b = rank_mask(topk_idx + t * k, k, E, magic); b; b &= b - 1)
             atomicAdd(&h[__builtin_ctzll(b)], 1);
     }
     __syncthreads();
@@ -85,7 +82,7 @@ __global__ __launch_bounds__(kHtTile) void ht_tile_hist_kernel(const int64_t* __
 constexpr int kHtStageRanks = 32;
 constexpr int kHtStagePitch = kHtStageRanks + 1;
 __global__ __launch_bounds__(kHtTile) void ht_rows_kernel(
-    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, int ntiles,
+    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, uint32_t magic, int ntiles,
     const int32_t* __restrict__ hist, int32_t* __restrict__ token_rank_row,
     int32_t* __restrict__ rank_offset) {
     __shared__ int32_t base[EP_MAX_RANKS];                 // first row of rank r for this tile
@@ -93,10 +90,9 @@ __global__ __launch_bounds__(kHtTile) void ht_rows_kernel(
     const int c = blockIdx.x;
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
-    const int epr = E / R;
     const int64_t t = static_cast<int64_t>(c) * kHtTile + threadIdx.x;
     const bool in = t < T;
-    const uint64_t m = in ? rank_mask(topk_idx + t * k, k, E, epr) : 0;
+    const uint64_t m = in ? rank_mask(topk_idx + t * k, k, E, magic) : 0;
 
     // Per rank: tokens in all tiles and in the tiles before this one.
     if (threadIdx.x < kWave) {
@@ -179,7 +175,7 @@ __global__ __launch_bounds__(256) void ht_meta_kernel(
     const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights,
     const int32_t* __restrict__ token_rank_row, int32_t* __restrict__ recv_src_idx,
     int64_t* __restrict__ recv_topk_idx, float* __restrict__ recv_w, int64_t T, int k, int E,
-    int R) {
+    int R, uint32_t magic) {
     const int epr = E / R;
     // T * k < 2^31 (checked by the API), so slot indices and their division by
     // k stay in 32 bits (a 64-bit division is a long software sequence here).
@@ -192,8 +188,8 @@ __global__ __launch_bounds__(256) void ht_meta_kernel(
         const int64_t* ids = topk_idx + static_cast<int64_t>(t) * k;
         const int64_t e = ids[j];
         const float wraw = (recv_w && topk_weights) ? topk_weights[i] : 0.0f;
-        uint64_t m = rank_mask(ids, k, E, epr);          // ranks the token reaches (R <= 64)
-        const int rj = (e >= 0 && e < E) ? rank_of(e, epr) : -1;
+        uint64_t m = rank_mask(ids, k, E, magic);        // ranks the token reaches (R <= 64)
+        const int rj = (e >= 0 && e < E) ? rank_of(e, magic) : -1;
         const int32_t* trr = token_rank_row + static_cast<int64_t>(t) * R;
         while (m) {
             // The rows of up to kIdBatch of the token's ranks, loaded together
@@ -235,7 +231,7 @@ typedef long long i64x2 __attribute__((ext_vector_type(2)));
 template <int KMAX, int NQ, bool kPairs>
 __global__ __launch_bounds__(kHtFusedThreads) void ht_fused_kernel(
     const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int64_t T,
-    int k, int E, int R, int ntiles, int32_t* __restrict__ token_rank_row,
+    int k, int E, int R, uint32_t magic, int ntiles, int32_t* __restrict__ token_rank_row,
     int32_t* __restrict__ recv_src_idx, int64_t* __restrict__ recv_topk_idx,
     float* __restrict__ recv_w, int32_t* __restrict__ rank_offset, const u32x4* __restrict__ pf_src,
     int64_t pf_vecs, uint32_t* __restrict__ pf_sink) {
@@ -261,8 +257,15 @@ __global__ __launch_bounds__(kHtFusedThreads) void ht_fused_kernel(
     // its own).
     const int wsl = threadIdx.x;                  // kHtFusedTile * KMAX <= kHtFusedThreads
     const float wreg = (want_w && wsl < nt * k) ? topk_weights[lo * k + wsl] : 0.0f;
-    // Sweep: lane r of every wave accumulates rank r's tokens (all / before the tile).
-    int my_all = 0, my_pre = 0;
+    // Sweep: per rank, the wave's tokens in all tiles and before this one,
+    // from one ballot per rank per step into wave-uniform (scalar)
+    // accumulators; lane r takes rank r's at the end.
+    int acc_all[kHtFusedMaxR], acc_pre[kHtFusedMaxR];
+#pragma unroll
+    for (int r = 0; r < kHtFusedMaxR; ++r) {
+        acc_all[r] = 0;
+        acc_pre[r] = 0;
+    }
     for (int64_t t0 = 0; t0 < T; t0 += static_cast<int64_t>(NQ) * kHtFusedThreads) {
         int64_t ids[NQ][KMAX];
 #pragma unroll
@@ -291,20 +294,27 @@ __global__ __launch_bounds__(kHtFusedThreads) void ht_fused_kernel(
             for (int j = 0; j < KMAX; ++j) {
                 const int64_t e = ids[q][j];
                 const bool valid = j < k && e >= 0 && e < E;
-                if (valid) m |= 1u << rank_of(e, epr);
+                if (valid) m |= 1u << rank_of(e, magic);
                 if (in_tile && j < k) tile_ids[(t - lo) * k + j] = valid ? static_cast<int32_t>(e) : -1;
             }
-            for (int r = 0; r < R; ++r) {
-                const bool bit = (m >> r) & 1u;
-                const int a = __popcll(ballot(bit));
-                const int p = __popcll(ballot(bit && t < lo));
-                if (lane == r) {
-                    my_all += a;
-                    my_pre += p;
+            const uint64_t before = ballot(t < lo);
+#pragma unroll
+            for (int r = 0; r < kHtFusedMaxR; ++r) {
+                if (r < R) {
+                    const uint64_t b = ballot((m >> r) & 1u);
+                    acc_all[r] += __popcll(b);
+                    acc_pre[r] += __popcll(b & before);
                 }
             }
         }
     }
+    int my_all = 0, my_pre = 0;
+#pragma unroll
+    for (int r = 0; r < kHtFusedMaxR; ++r)
+        if (lane == r) {
+            my_all = acc_all[r];
+            my_pre = acc_pre[r];
+        }
     if (lane < R) {
         cnt_all[wave][lane] = my_all;
         cnt_pre[wave][lane] = my_pre;
@@ -336,7 +346,7 @@ __global__ __launch_bounds__(kHtFusedThreads) void ht_fused_kernel(
         if (lane < nt)
             for (int j = 0; j < k; ++j) {
                 const int e = tile_ids[lane * k + j];
-                if (e >= 0) m |= 1u << rank_of(e, epr);
+                if (e >= 0) m |= 1u << rank_of(e, magic);
             }
         for (int r = 0; r < R; ++r) {
             const uint64_t b = ballot((m >> r) & 1u);
@@ -356,7 +366,7 @@ __global__ __launch_bounds__(kHtFusedThreads) void ht_fused_kernel(
             const int row = tile_row[tl * R + r];
             if (row < 0) continue;
             const int e = tile_ids[tl * k + j];
-            const bool local = e >= 0 && rank_of(e, epr) == r;
+            const bool local = e >= 0 && rank_of(e, magic) == r;
             recv_topk_idx[static_cast<int64_t>(row) * k + j] = local ? e - r * epr : -1;
             if (recv_w) recv_w[static_cast<int64_t>(row) * k + j] = (local && want_w) ? tile_w[tl * k + j] : 0.0f;
             if (j == 0) recv_src_idx[row] = static_cast<int32_t>(lo + tl);
@@ -377,7 +387,7 @@ constexpr int kHtSmallThreads = 512;
 constexpr int kHtSmallWaves = kHtSmallThreads / kWave;
 __global__ __launch_bounds__(kHtSmallThreads) void ht_small_kernel(
     const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
-    const float* __restrict__ topk_weights, int64_t T, int k, int E, int R, int V, int segs,
+    const float* __restrict__ topk_weights, int64_t T, int k, int E, int R, uint32_t magic, int V, int segs,
     u32x4* __restrict__ recv, int32_t* __restrict__ token_rank_row,
     int32_t* __restrict__ recv_src_idx, int64_t* __restrict__ recv_topk_idx,
     float* __restrict__ recv_w, int32_t* __restrict__ rank_offset) {
@@ -399,7 +409,7 @@ __global__ __launch_bounds__(kHtSmallThreads) void ht_small_kernel(
         val[u] = x[t * V + (v < V ? v : V - 1)];
     }
     // Sweep: thread i takes token i (T <= kHtSmallThreads).
-    const uint64_t m = tid < T ? rank_mask(topk_idx + static_cast<int64_t>(tid) * k, k, E, epr) : 0;
+    const uint64_t m = tid < T ? rank_mask(topk_idx + static_cast<int64_t>(tid) * k, k, E, magic) : 0;
     int my_all = 0, my_pre = 0;
     for (int r = 0; r < R; ++r) {
         const bool bit = (m >> r) & 1u;
@@ -462,7 +472,7 @@ __global__ __launch_bounds__(kHtSmallThreads) void ht_small_kernel(
         const int row = rows[r];
         if (row < 0) continue;
         const int64_t e = topk_idx[t * k + j];
-        const bool local = e >= 0 && e < E && rank_of(e, epr) == r;
+        const bool local = e >= 0 && e < E && rank_of(e, magic) == r;
         recv_topk_idx[static_cast<int64_t>(row) * k + j] = local ? e - static_cast<int64_t>(r) * epr : -1;
         if (recv_w) recv_w[static_cast<int64_t>(row) * k + j] = (local && want_w) ? topk_weights[t * k + j] : 0.0f;
         if (j == 0) recv_src_idx[row] = static_cast<int32_t>(t);
@@ -489,14 +499,15 @@ hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const floa
         hipLaunchKernelGGL(ht_zero_offsets_kernel, dim3(1), dim3(2 * kWave), 0, stream, rank_offset, R);
         return hipGetLastError();
     }
+    const uint32_t magic = rank_magic(E / R);
     const int64_t small_segs = ceil_div(H / 8, kCopyVec * kWave);
     if (T <= kHtSmallThreads && T * k <= kSmallSlots &&
         T * small_segs * kHtSmallThreads <= kMaxLaunchThreads) {
         const int V = H / 8;
         const int segs = static_cast<int>(small_segs);
         hipLaunchKernelGGL(ht_small_kernel, dim3(static_cast<unsigned>(T * segs)), dim3(kHtSmallThreads),
-                           0, stream, static_cast<const u32x4*>(x), topk_idx, topk_weights, T, k, E, R, V,
-                           segs, static_cast<u32x4*>(recv_x), token_rank_row, recv_src_idx,
+                           0, stream, static_cast<const u32x4*>(x), topk_idx, topk_weights, T, k, E, R, magic,
+                           V, segs, static_cast<u32x4*>(recv_x), token_rank_row, recv_src_idx,
                            recv_topk_idx, recv_w, rank_offset);
         return hipGetLastError();
     }
@@ -509,7 +520,7 @@ hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const floa
         auto kern = k <= 8 ? (pairs ? ht_fused_kernel<8, 1, true> : ht_fused_kernel<8, 1, false>)
                            : (pairs ? ht_fused_kernel<16, 1, true> : ht_fused_kernel<16, 1, false>);
         hipLaunchKernelGGL(kern, dim3(ntiles + pf_blocks), dim3(kHtFusedThreads), 0, stream, topk_idx,
-                           topk_weights, T, k, E, R, ntiles, token_rank_row, recv_src_idx,
+                           topk_weights, T, k, E, R, magic, ntiles, token_rank_row, recv_src_idx,
                            recv_topk_idx, recv_w, rank_offset, static_cast<const u32x4*>(x),
                            pf_bytes / 16, static_cast<uint32_t*>(workspace));
         const hipError_t e = hipGetLastError();
@@ -519,15 +530,15 @@ hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const floa
     const int ntiles = static_cast<int>(ceil_div(T, kHtTile));
     int32_t* hist = static_cast<int32_t*>(workspace);
     hipLaunchKernelGGL(ht_tile_hist_kernel, dim3(ntiles), dim3(kHtTile), 0, stream, topk_idx, T, k,
-                       E, R, hist);
+                       E, R, magic, hist);
     hipLaunchKernelGGL(ht_rows_kernel, dim3(ntiles), dim3(kHtTile), 0, stream, topk_idx, T, k, E,
-                       R, ntiles, hist, token_rank_row, rank_offset);
+                       R, magic, ntiles, hist, token_rank_row, rank_offset);
     const int64_t n = T * k;                          // one thread per (token, slot)
     const int64_t blocks = ceil_div(n, 256);
     const int64_t cap = kMaxLaunchThreads / 256;
     hipLaunchKernelGGL(ht_meta_kernel, dim3(static_cast<unsigned>(blocks < cap ? blocks : cap)),
                        dim3(256), 0, stream, topk_idx, topk_weights, token_rank_row, recv_src_idx,
-                       recv_topk_idx, recv_w, T, k, E, R);
+                       recv_topk_idx, recv_w, T, k, E, R, magic);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_dispatch_copy_bf16(x, token_rank_row, recv_x, T * R, T, H, R, stream);

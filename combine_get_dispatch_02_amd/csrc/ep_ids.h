@@ -25,4 +25,22 @@ __device__ __forceinline__ void load_ids(const int64_t* __restrict__ ids, int j0
         if (j0 + u >= k) v[u] = -1;
 }
 
+// The rank of a valid expert id, e / epr (epr = E / R experts per rank), as
+// one multiply-high instead of the ~10 instructions of a 32-bit division:
+// with magic = ceil(2^32 / epr) for epr >= 2, write magic * epr = 2^32 + d,
+// 0 <= d < epr; then e * magic / 2^32 = e / epr + e * d / (epr * 2^32), and
+// the excess stays below 1 / epr -- so the floor is unchanged -- whenever
+// e * epr < 2^32, which 0 <= e < E <= 2048 guarantees.  epr == 1 has
+// magic 0: every expert is its own rank.
+inline uint32_t rank_magic(int epr) {
+    if (epr <= 1) return 0u;
+    return static_cast<uint32_t>(((uint64_t(1) << 32) + static_cast<uint64_t>(epr) - 1) /
+                                 static_cast<uint64_t>(epr));
+}
+
+__device__ __forceinline__ int rank_of(int64_t e, uint32_t magic) {
+    const uint32_t u = static_cast<uint32_t>(e);
+    return static_cast<int>(magic ? __umulhi(u, magic) : u);
+}
+
 }  // namespace ep

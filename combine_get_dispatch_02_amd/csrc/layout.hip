@@ -25,13 +25,12 @@ namespace {
 // its histograms are the final counts and no reduce launch follows.
 template <bool kFinal>
 __global__ __launch_bounds__(kLayoutTokensPerBlock) void layout_partial_kernel(
-    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, int P,
+    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, int P, uint32_t magic,
     uint8_t* __restrict__ in_rank, int32_t* __restrict__ partial,
     int32_t* __restrict__ per_expert, int32_t* __restrict__ per_rank,
     int32_t* __restrict__ per_group) {
     extern __shared__ int32_t lds[];
     const int G = R / P;
-    const int epr = E / R;
     const int nh = E + R + G;
     int32_t* h_e = lds;
     int32_t* h_r = lds + E;
@@ -54,8 +53,7 @@ __global__ __launch_bounds__(kLayoutTokensPerBlock) void layout_partial_kernel(
                 const int64_t e = v[u];
                 if (e >= 0 && e < E) {
                     atomicAdd(&h_e[e], 1);
-                    // 0 <= e < E: a 32-bit division (64-bit is a long software sequence)
-                    m |= uint64_t(1) << (static_cast<uint32_t>(e) / static_cast<uint32_t>(epr));
+                    m |= uint64_t(1) << rank_of(e, magic);   // magic = rank_magic(E / R)
                 }
             }
         }
@@ -139,14 +137,14 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int k, int E, int R
                        kLayoutTokensPerBlock * sizeof(uint64_t);
     if (nblk == 1) {
         hipLaunchKernelGGL(layout_partial_kernel<true>, dim3(1), dim3(kLayoutTokensPerBlock), lds,
-                           stream, topk_idx, T, k, E, R, P, in_rank, partial, per_expert, per_rank,
-                           per_group);
+                           stream, topk_idx, T, k, E, R, P, rank_magic(E / R), in_rank, partial,
+                           per_expert, per_rank, per_group);
         return hipGetLastError();
     }
     if (nblk > 0) {
         hipLaunchKernelGGL(layout_partial_kernel<false>, dim3(static_cast<unsigned>(nblk)),
                            dim3(kLayoutTokensPerBlock), lds, stream, topk_idx, T, k, E, R, P,
-                           in_rank, partial, per_expert, per_rank, per_group);
+                           rank_magic(E / R), in_rank, partial, per_expert, per_rank, per_group);
     }
     hipLaunchKernelGGL(layout_reduce_kernel, dim3(static_cast<unsigned>(ceil_div(nh, 256))),
                        dim3(256), 0, stream, partial, static_cast<int>(nblk), E, R, G, per_expert,
