@@ -245,8 +245,9 @@ __global__ __launch_bounds__(kHtFusedThreads) void ht_fused_kernel(
     __shared__ int32_t tile_ids[kHtFusedTile * kHtFusedMaxK];   // -1 for an empty slot
     __shared__ float tile_w[kHtFusedTile * kHtFusedMaxK];
     __shared__ int32_t tile_row[kHtFusedTile * kHtFusedMaxR];
+    __shared__ uint32_t rank_bit[EP_MAX_EXPERTS + 1];
     const int lane = lane_id();
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int epr = E / R;
     const int64_t lo = static_cast<int64_t>(blockIdx.x) * kHtFusedTile;
     const int nt = static_cast<int>(T - lo < kHtFusedTile ? T - lo : kHtFusedTile);
@@ -257,6 +258,12 @@ __global__ __launch_bounds__(kHtFusedThreads) void ht_fused_kernel(
     // its own).
     const int wsl = threadIdx.x;                  // kHtFusedTile * KMAX <= kHtFusedThreads
     const float wreg = (want_w && wsl < nt * k) ? topk_weights[lo * k + wsl] : 0.0f;
+    // rank_bit[e] = 1 << (rank of expert e); rank_bit[E] = 0 stands for
+    // every invalid id (any value outside [0, E), read as unsigned): one LDS
+    // read per id builds a token's rank mask.
+    for (int e = threadIdx.x; e <= E; e += kHtFusedThreads)
+        rank_bit[e] = e < E ? 1u << rank_of(e, magic) : 0u;
+    const uint64_t uE = static_cast<uint64_t>(E);
     // Sweep: per rank, the wave's tokens in all tiles and before this one,
     // from one ballot per rank per step into wave-uniform (scalar)
     // accumulators; lane r takes rank r's at the end.
@@ -266,6 +273,7 @@ __global__ __launch_bounds__(kHtFusedThreads) void ht_fused_kernel(
         acc_all[r] = 0;
         acc_pre[r] = 0;
     }
+    __syncthreads();
     for (int64_t t0 = 0; t0 < T; t0 += static_cast<int64_t>(NQ) * kHtFusedThreads) {
         int64_t ids[NQ][KMAX];
 #pragma unroll
@@ -287,23 +295,29 @@ __global__ __launch_bounds__(kHtFusedThreads) void ht_fused_kernel(
         }
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            const int64_t t = t0 + q * kHtFusedThreads + threadIdx.x;
-            const bool in_tile = t >= lo && t < lo + nt;
+            // A wave's 64 tokens start at a multiple of 64, as the tile does,
+            // so "in the tile" and "before the tile" hold for the whole wave.
+            const int64_t wt0 = t0 + q * kHtFusedThreads + static_cast<int64_t>(wave) * kWave;
             uint32_t m = 0;
 #pragma unroll
             for (int j = 0; j < KMAX; ++j) {
-                const int64_t e = ids[q][j];
-                const bool valid = j < k && e >= 0 && e < E;
-                if (valid) m |= 1u << rank_of(e, magic);
-                if (in_tile && j < k) tile_ids[(t - lo) * k + j] = valid ? static_cast<int32_t>(e) : -1;
+                const uint64_t u = static_cast<uint64_t>(ids[q][j]);   // slots j >= k hold -1
+                m |= rank_bit[u < uE ? u : uE];
             }
-            const uint64_t before = ballot(t < lo);
+            if (wt0 == lo && lane < nt) {
+#pragma unroll
+                for (int j = 0; j < KMAX; ++j) {
+                    const uint64_t u = static_cast<uint64_t>(ids[q][j]);
+                    if (j < k) tile_ids[lane * k + j] = u < uE ? static_cast<int32_t>(u) : -1;
+                }
+            }
+            const bool wave_before = wt0 < lo;
 #pragma unroll
             for (int r = 0; r < kHtFusedMaxR; ++r) {
                 if (r < R) {
-                    const uint64_t b = ballot((m >> r) & 1u);
-                    acc_all[r] += __popcll(b);
-                    acc_pre[r] += __popcll(b & before);
+                    const int c = __popcll(ballot((m >> r) & 1u));
+                    acc_all[r] += c;
+                    if (wave_before) acc_pre[r] += c;
                 }
             }
         }

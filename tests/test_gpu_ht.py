@@ -160,6 +160,22 @@ def test_ht_edge_shapes(T, k, E, R, H):
     run_case(x, idx, None, E, R)
 
 
+@pytest.mark.parametrize("T,k,E,R", [(200, 6, 24, 6), (3000, 8, 64, 8), (3001, 7, 64, 8),
+                                     (5000, 6, 64, 32)])
+def test_ht_ids_with_high_word_set(T, k, E, R):
+    """Ids outside [0, E) whose low 32-bit word is a valid expert are empty
+    slots, on the small-batch, one-launch (paired and single id loads) and
+    three-launch index paths."""
+    rng = np.random.default_rng(T * k)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int64)
+    bad = rng.random((T, k)) < 0.15
+    vals = np.array([2 ** 32, 2 ** 32 + 3, -(2 ** 32), 2 ** 40 + 1, -(2 ** 63) + 2, 2 ** 62 + 5], dtype=np.int64)
+    idx[bad] = rng.choice(vals, size=int(bad.sum()))
+    x = rng.integers(0, 0x7F00, size=(T, 64)).astype(np.uint16)
+    w = rng.random((T, k)).astype(np.float32)
+    run_case(x, idx, w, E, R)
+
+
 @pytest.mark.parametrize("T,k,ids_off", [(300, 8, 0), (300, 8, 1), (129, 16, 0), (129, 16, 1),
                                          (129, 6, 0), (1001, 2, 0), (77, 4, 0), (77, 4, 1)])
 def test_ht_id_alignment(T, k, ids_off):

@@ -300,6 +300,24 @@ def test_edge_duplicates_and_out_of_range_ids():
     _run_small(idx, x, w, E, 6, 2)
 
 
+# Ids outside [0, E) whose low 32-bit word is a valid expert (2^32 + e, a
+# negative value with low word e): empty slots like -1, on the single-launch
+# (T*k <= 2048), fused (<= 2^15 slots) and two-launch receive-order paths.
+HIGH_WORD_IDS = [2 ** 32, 2 ** 32 + 3, -(2 ** 32), 2 ** 40 + 1, -(2 ** 63) + 2, 2 ** 62 + 5]
+
+
+@pytest.mark.parametrize("T,k,E,R", [(200, 6, 24, 6), (3000, 8, 64, 8), (9000, 6, 64, 8)])
+def test_edge_ids_with_high_word_set(T, k, E, R):
+    rng = np.random.default_rng(T + k)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int64)
+    bad = rng.random((T, k)) < 0.15
+    idx[bad] = rng.choice(np.array(HIGH_WORD_IDS, dtype=np.int64), size=int(bad.sum()))
+    x = rng.integers(0, 0x7F00, size=(T, 64)).astype(np.uint16)
+    w = rng.standard_normal((T, k)).astype(np.float32)
+    _, ref_d = _run_small(idx, x, w, E, R, 2)
+    assert int(ref_d["recv_expert_offset"][-1]) == int((~bad).sum())
+
+
 @pytest.mark.parametrize("T,k,E,R,H", [(1, 1, 1, 1, 8), (5, 1, 4, 4, 8), (64, 2, 2, 1, 24),
                                        (257, 8, 64, 64, 64), (1000, 3, 2048, 64, 16),
                                        (100, 16, 64, 8, 136),     # single-launch path, k > 8
