@@ -12,29 +12,26 @@
 // Up to 16384 tokens, 16 ranks and top-16: two launches, deterministic, no
 // global atomics:
 //   ht_fused      one block of 1024 threads per 64-token tile: every block
-//                 sweeps all tokens' rank masks (one token per thread per
-//                 step) and counts, per rank, the tokens before
-//                 its tile and in all, with one ballot per rank per wave (no
-//                 atomics); a scan over ranks gives recv_rank_offset and the
-//                 tile's base rows; one wave ranks the tile's tokens by
-//                 ballots; token_rank_row and each row's source token and
-//                 remapped ids and weights are written from LDS, one token
-//                 per wave.  Extra blocks read x through the caches meanwhile
-//                 (see prefetch_vectors).
+//                 sweeps all tokens (one token per thread per step), builds
+//                 each token's rank mask from an LDS table of rank bits, and
+//                 counts, per rank, the tokens before its tile and in all,
+//                 with one ballot per rank per wave (no atomics); a scan over
+//                 ranks gives recv_rank_offset and the tile's base rows; one
+//                 wave ranks the tile's tokens by ballots; token_rank_row and
+//                 each row's source token and remapped ids and weights are
+//                 written from LDS, one token per wave.  Extra blocks read x
+//                 through the caches meanwhile (see prefetch_vectors).
 //   copy          as below.
-// Otherwise four launches:
-//   ht_tile_hist  one token per thread, 256 tokens per tile: the token's rank
+// Otherwise three launches:
+//   ht_tile_hist  one token per thread, 128 tokens per tile: the token's rank
 //                 mask (R <= 64) from its k ids; per-tile, per-rank counts
-//   ht_rows       per tile: per-rank prefix over earlier tiles, a 64-lane scan
-//                 over ranks (-> recv_rank_offset), then the rank of each token
-//                 among the tile's tokens routed to the same rank from one
-//                 ballot per rank per wave; writes token_rank_row
-//   ht_meta       each row's source token and remapped top-k ids and weights,
-//                 one thread per (token, slot): from the token's rank mask,
-//                 the thread writes its slot's entry of every row the token
-//                 has, so the k threads of a token store each row's k entries
-//                 together (coalesced), with no thread per unused (token,
-//                 rank) pair
+//   ht_rows       per tile: per-rank sums over all tiles and the earlier ones,
+//                 a 64-lane scan over ranks (-> recv_rank_offset), the rank of
+//                 each token among the tile's tokens routed to the same rank
+//                 from one ballot per rank per wave; writes token_rank_row and
+//                 each row's source token and remapped top-k ids and weights
+//                 (one thread per (token, slot): the k threads of a token
+//                 store each row's k entries together)
 //   copy          the bf16 copy kernel of ep_dispatch, driven by the [T, R]
 //                 map token_rank_row instead of the [T, k] token_row
 #include "../../include/ep.h"
@@ -45,9 +42,9 @@
 namespace ep {
 namespace {
 
-constexpr int kHtTile = 256;          // tokens per tile = threads per block
+constexpr int kHtTile = 128;          // tokens per tile of the multi-launch path
 constexpr int kHtWaves = kHtTile / kWave;
-constexpr int kHtHistBatch = 64;
+constexpr int kHtRowsThreads = 512;   // threads per ht_rows block (kHtWaves of them own the tokens)
 
 // Ranks of valid expert ids: rank_of (ep_ids.h), a multiply-high by
 // magic = rank_magic(E / R).
@@ -81,135 +78,174 @@ __global__ __launch_bounds__(kHtTile) void ht_tile_hist_kernel(const int64_t* __
 
 constexpr int kHtStageRanks = 32;
 constexpr int kHtStagePitch = kHtStageRanks + 1;
-__global__ __launch_bounds__(kHtTile) void ht_rows_kernel(
-    const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int R, uint32_t magic, int ntiles,
-    const int32_t* __restrict__ hist, int32_t* __restrict__ token_rank_row,
-    int32_t* __restrict__ rank_offset) {
-    __shared__ int32_t base[EP_MAX_RANKS];                 // first row of rank r for this tile
-    __shared__ int32_t wcnt[kHtWaves][EP_MAX_RANKS];       // per-wave counts -> offsets
+constexpr int kHtHistLoads = 16;      // tile histogram entries per thread per round trip
+constexpr int kHtRecBatch = 8;        // slots whose ids a thread loads per round trip
+// Second launch of the multi-launch path: one block of kHtRowsThreads
+// threads per tile of kHtTile tokens, thread t < kHtTile owning token t.
+//   1. Per rank: its tokens in all tiles (-> recv_rank_offset) and in the
+//      tiles before this one, summed from the per-tile histograms by
+//      kHtRowsThreads / R threads per rank (kHtHistLoads loads each per round
+//      trip, requested together with the tile's ids), then over those threads
+//      in LDS, then scanned over ranks by one wave.
+//   2. The rank of each token among the tile's tokens routed to the same
+//      rank: one ballot per rank per token wave.
+//   3. Per chunk of up to 32 ranks: the rows go to LDS (pitch 33 words: no
+//      bank conflicts), then out to token_rank_row in order (contiguous when
+//      R <= 32, 128-byte runs per token otherwise), and each row's records
+//      -- source token, the k remapped ids and weights -- are written by one
+//      thread per (token, slot): k consecutive threads store a row's k
+//      entries together.  The record stores are most of the launch's time,
+//      hence the threads beyond the tile's tokens: at 32768 tokens x top-8
+//      over 32 ranks the launch takes 16.6 us with 128-token tiles of 512
+//      threads, against 24.1 us with 256-token tiles of 256 threads and
+//      17.2-20.4 us for 64/128/256-token tiles of 256-1024 threads (kernel
+//      trace); without the records it took 13.5 us, and the former separate
+//      records launch 9.5 us.
+__global__ __launch_bounds__(kHtRowsThreads) void ht_rows_kernel(
+    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int64_t T, int k,
+    int E, int R, uint32_t magic, uint32_t kmagic, int ntiles, const int32_t* __restrict__ hist,
+    int32_t* __restrict__ token_rank_row, int32_t* __restrict__ rank_offset,
+    int32_t* __restrict__ recv_src_idx, int64_t* __restrict__ recv_topk_idx,
+    float* __restrict__ recv_w) {
+    __shared__ int32_t wcnt[kHtWaves][EP_MAX_RANKS];       // per-wave counts -> first rows
+    __shared__ int32_t part_tot[kHtRowsThreads], part_pre[kHtRowsThreads];
+    __shared__ uint64_t tok_mask[kHtTile];
+    __shared__ int32_t stage[kHtTile * kHtStagePitch];
     const int c = blockIdx.x;
+    const int tid = static_cast<int>(threadIdx.x);
     const int lane = lane_id();
-    const int wave = threadIdx.x / kWave;
-    const int64_t t = static_cast<int64_t>(c) * kHtTile + threadIdx.x;
-    const bool in = t < T;
-    const uint64_t m = in ? rank_mask(topk_idx + t * k, k, E, magic) : 0;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int epr = E / R;
+    const int64_t t0 = static_cast<int64_t>(c) * kHtTile;
+    const int nt = static_cast<int>(T - t0 < kHtTile ? T - t0 : kHtTile);
 
-    // Per rank: tokens in all tiles and in the tiles before this one.
-    if (threadIdx.x < kWave) {
-        const int r = lane;
-        int tot = 0, pre = 0;
-        if (r < R) {
-            for (int c0 = 0; c0 < ntiles; c0 += kHtHistBatch) {
-                int v[kHtHistBatch];
+    // 1. Histogram sums: thread (g, r) = (tid / R, tid % R) takes tiles g, g + G, ...
+    const int G = kHtRowsThreads / R;
+    const int hr = tid % R;
+    const int hg = tid / R;
+    int tot = 0, pre = 0;
+    int hv[kHtHistLoads];
+    const bool summer = hg < G;
+    int c0 = hg;
 #pragma unroll
-                for (int i = 0; i < kHtHistBatch; ++i)
-                    v[i] = (c0 + i < ntiles) ? hist[static_cast<int64_t>(c0 + i) * R + r] : 0;
+    for (int i = 0; i < kHtHistLoads; ++i) {
+        const int cc = c0 + i * G;
+        hv[i] = (summer && cc < ntiles) ? hist[static_cast<int64_t>(cc) * R + hr] : 0;
+    }
+    const int64_t t = t0 + tid;
+    const uint64_t m = (tid < kHtTile && t < T) ? rank_mask(topk_idx + t * k, k, E, magic) : 0;
+    if (tid < kHtTile) tok_mask[tid] = m;
+    for (;;) {
 #pragma unroll
-                for (int i = 0; i < kHtHistBatch; ++i) {
-                    tot += v[i];
-                    pre += (c0 + i < c) ? v[i] : 0;
-                }
-            }
+        for (int i = 0; i < kHtHistLoads; ++i) {
+            const int cc = c0 + i * G;
+            tot += hv[i];
+            pre += cc < c ? hv[i] : 0;
         }
+        c0 += kHtHistLoads * G;
+        if (!summer || c0 >= ntiles) break;
+#pragma unroll
+        for (int i = 0; i < kHtHistLoads; ++i) {
+            const int cc = c0 + i * G;
+            hv[i] = cc < ntiles ? hist[static_cast<int64_t>(cc) * R + hr] : 0;
+        }
+    }
+    part_tot[tid] = summer ? tot : 0;
+    part_pre[tid] = summer ? pre : 0;
+    // 2. In-tile ranks: one ballot per rank per token wave.
+    if (wave < kHtWaves)
+        for (int r = 0; r < R; ++r) {
+            const uint64_t b = ballot((m >> r) & 1);
+            if (lane == 0) wcnt[wave][r] = __popcll(b);
+        }
+    __syncthreads();
+    if (tid < kWave) {
+        const int r = lane;
+        int rt = 0, rp = 0;
+        if (r < R)
+            for (int g = 0; g < G; ++g) {
+                rt += part_tot[g * R + r];
+                rp += part_pre[g * R + r];
+            }
         // exclusive scan of the totals over ranks (one lane per rank)
-        int incl = tot;
+        int incl = rt;
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) {
             const int u = __shfl_up(incl, off, kWave);
             if (lane >= off) incl += u;
         }
-        const int excl = incl - tot;
-        if (r < R) base[r] = excl + pre;
+        const int excl = incl - rt;
+        if (r < R) {
+            int run = excl + rp;
+            for (int w = 0; w < kHtWaves; ++w) {
+                const int v = wcnt[w][r];
+                wcnt[w][r] = run;
+                run += v;
+            }
+        }
         if (c == 0) {
             if (r < R) rank_offset[r] = excl;
             if (r == R - 1) rank_offset[R] = incl;
         }
     }
-    // In-tile ranks: one ballot per rank per wave.
-    for (int r = 0; r < R; ++r) {
-        const uint64_t b = ballot((m >> r) & 1);
-        if (lane == 0) wcnt[wave][r] = __popcll(b);
-    }
     __syncthreads();
-    if (threadIdx.x < R) {
-        int run = base[threadIdx.x];
-        for (int w = 0; w < kHtWaves; ++w) {
-            const int v = wcnt[w][threadIdx.x];
-            wcnt[w][threadIdx.x] = run;
-            run += v;
-        }
-    }
-    __syncthreads();
-    // Rows of the tile's tokens, up to 32 ranks at a time: ranked by ballot
-    // into LDS (row pitch 33 words: no bank conflicts), then written out in
-    // order, so the tile's part of token_rank_row (contiguous when R <= 32,
-    // 128-byte runs per token otherwise) is stored coalesced.  Lanes past the
-    // last token have m == 0 and add nothing to a ballot.
-    __shared__ int32_t stage[kHtTile * kHtStagePitch];
-    const int64_t t0 = static_cast<int64_t>(c) * kHtTile;
-    const int nt = static_cast<int>(T - t0 < kHtTile ? T - t0 : kHtTile);
+    // 3. Rows, up to 32 ranks at a time.  Lanes past the last token have
+    // m == 0 and add nothing to a ballot.
+    const bool want_w = recv_w != nullptr && topk_weights != nullptr;
     for (int r0 = 0; r0 < R; r0 += kHtStageRanks) {
         const int nr = R - r0 < kHtStageRanks ? R - r0 : kHtStageRanks;
-        for (int rr = 0; rr < nr; ++rr) {
-            const int r = r0 + rr;
-            const uint64_t b = ballot((m >> r) & 1);
-            int row = -1;
-            if ((m >> r) & 1) row = wcnt[wave][r] + __popcll(b & lanes_below());
-            stage[threadIdx.x * kHtStagePitch + rr] = row;
-        }
+        if (wave < kHtWaves)
+            for (int rr = 0; rr < nr; ++rr) {
+                const int r = r0 + rr;
+                const uint64_t b = ballot((m >> r) & 1);
+                int row = -1;
+                if ((m >> r) & 1) row = wcnt[wave][r] + __popcll(b & lanes_below());
+                stage[tid * kHtStagePitch + rr] = row;
+            }
         __syncthreads();
-        for (int i = threadIdx.x; i < nt * nr; i += kHtTile) {
+        for (int i = tid; i < nt * nr; i += kHtRowsThreads) {
             const int tl = i / nr;
             const int rr = i - tl * nr;
             token_rank_row[(t0 + tl) * R + r0 + rr] = stage[tl * kHtStagePitch + rr];
         }
-        __syncthreads();
-    }
-}
-
-
-// Per-row records: one thread per (token t, rank r, top-k slot j), k
-// consecutive threads per (t, r), so the k ids and weights of a row go out as
-// one contiguous store per wave.
-__global__ __launch_bounds__(256) void ht_meta_kernel(
-    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights,
-    const int32_t* __restrict__ token_rank_row, int32_t* __restrict__ recv_src_idx,
-    int64_t* __restrict__ recv_topk_idx, float* __restrict__ recv_w, int64_t T, int k, int E,
-    int R, uint32_t magic) {
-    const int epr = E / R;
-    // T * k < 2^31 (checked by the API), so slot indices and their division by
-    // k stay in 32 bits (a 64-bit division is a long software sequence here).
-    const uint32_t n = static_cast<uint32_t>(T * k);
-    const uint32_t uk = static_cast<uint32_t>(k);
-    const uint32_t stride = gridDim.x * blockDim.x;
-    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        const uint32_t t = i / uk;
-        const int j = static_cast<int>(i - t * uk);
-        const int64_t* ids = topk_idx + static_cast<int64_t>(t) * k;
-        const int64_t e = ids[j];
-        const float wraw = (recv_w && topk_weights) ? topk_weights[i] : 0.0f;
-        uint64_t m = rank_mask(ids, k, E, magic);        // ranks the token reaches (R <= 64)
-        const int rj = (e >= 0 && e < E) ? rank_of(e, magic) : -1;
-        const int32_t* trr = token_rank_row + static_cast<int64_t>(t) * R;
-        while (m) {
-            // The rows of up to kIdBatch of the token's ranks, loaded together
-            // (rank 0 stands in for a missing one, and is not used).
-            int rr[kIdBatch], row[kIdBatch];
+        // Records of the chunk's rows: thread i takes slot j of token tl, for
+        // every rank of the chunk that the token reaches.
+        // The slots' ids and weights are loaded kHtRecBatch at a time (the
+        // tile's slots are contiguous; indices clamped, not branched on), so
+        // one round trip serves kHtRecBatch slots.
+        const uint64_t chunk = nr == 64 ? ~uint64_t(0) : ((uint64_t(1) << nr) - 1);
+        const int ns = nt * k;
+        const int64_t s0 = t0 * k;
+        for (int i0 = tid; i0 < ns; i0 += kHtRowsThreads * kHtRecBatch) {
+            int64_t ev[kHtRecBatch];
+            float wv[kHtRecBatch];
 #pragma unroll
-            for (int u = 0; u < kIdBatch; ++u) {
-                rr[u] = m ? __builtin_ctzll(m) : -1;
-                m &= m - 1;
-                row[u] = trr[rr[u] >= 0 ? rr[u] : 0];
+            for (int u = 0; u < kHtRecBatch; ++u) {
+                const int i = i0 + u * kHtRowsThreads;
+                const int64_t gs = s0 + (i < ns ? i : ns - 1);
+                ev[u] = topk_idx[gs];
+                wv[u] = want_w ? topk_weights[gs] : 0.0f;
             }
 #pragma unroll
-            for (int u = 0; u < kIdBatch; ++u) {
-                if (rr[u] < 0 || row[u] < 0) continue;
-                const bool local = rr[u] == rj;
-                recv_topk_idx[static_cast<int64_t>(row[u]) * k + j] = local ? e - static_cast<int64_t>(rr[u]) * epr : -1;
-                if (recv_w) recv_w[static_cast<int64_t>(row[u]) * k + j] = local ? wraw : 0.0f;
-                if (j == 0) recv_src_idx[row[u]] = static_cast<int32_t>(t);
+            for (int u = 0; u < kHtRecBatch; ++u) {
+                const int i = i0 + u * kHtRowsThreads;
+                if (i >= ns) break;
+                const uint32_t tl = kmagic ? __umulhi(static_cast<uint32_t>(i), kmagic) : static_cast<uint32_t>(i);
+                const int j = i - static_cast<int>(tl) * k;
+                const int64_t e = ev[u];
+                const int rj = (e >= 0 && e < E) ? rank_of(e, magic) : -1;
+                for (uint64_t mm = (tok_mask[tl] >> r0) & chunk; mm; mm &= mm - 1) {
+                    const int rr = __builtin_ctzll(mm);
+                    const int row = stage[tl * kHtStagePitch + rr];
+                    const int r = r0 + rr;
+                    const bool local = r == rj;
+                    recv_topk_idx[static_cast<int64_t>(row) * k + j] = local ? e - static_cast<int64_t>(r) * epr : -1;
+                    if (recv_w) recv_w[static_cast<int64_t>(row) * k + j] = local ? wv[u] : 0.0f;
+                    if (j == 0) recv_src_idx[row] = static_cast<int32_t>(t0 + tl);
+                }
             }
         }
+        __syncthreads();
     }
 }
 
@@ -545,14 +581,9 @@ hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const floa
     int32_t* hist = static_cast<int32_t*>(workspace);
     hipLaunchKernelGGL(ht_tile_hist_kernel, dim3(ntiles), dim3(kHtTile), 0, stream, topk_idx, T, k,
                        E, R, magic, hist);
-    hipLaunchKernelGGL(ht_rows_kernel, dim3(ntiles), dim3(kHtTile), 0, stream, topk_idx, T, k, E,
-                       R, magic, ntiles, hist, token_rank_row, rank_offset);
-    const int64_t n = T * k;                          // one thread per (token, slot)
-    const int64_t blocks = ceil_div(n, 256);
-    const int64_t cap = kMaxLaunchThreads / 256;
-    hipLaunchKernelGGL(ht_meta_kernel, dim3(static_cast<unsigned>(blocks < cap ? blocks : cap)),
-                       dim3(256), 0, stream, topk_idx, topk_weights, token_rank_row, recv_src_idx,
-                       recv_topk_idx, recv_w, T, k, E, R, magic);
+    hipLaunchKernelGGL(ht_rows_kernel, dim3(ntiles), dim3(kHtRowsThreads), 0, stream, topk_idx,
+                       (recv_w ? topk_weights : nullptr), T, k, E, R, magic, rank_magic(k), ntiles,
+                       hist, token_rank_row, rank_offset, recv_src_idx, recv_topk_idx, recv_w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_dispatch_copy_bf16(x, token_rank_row, recv_x, T * R, T, H, R, stream);
