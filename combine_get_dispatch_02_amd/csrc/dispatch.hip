@@ -358,6 +358,8 @@ __global__ __launch_bounds__(kFusedThreads) void rows_fused_kernel(
     // Addresses are a scalar base plus a 32-bit byte offset (one VGPR of
     // address per load).
     const char* ids_base = reinterpret_cast<const char*>(topk_idx);
+    const uint64_t uE = static_cast<uint64_t>(E);     // valid: an id below E read as unsigned
+    const unsigned wv = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave));
     if (kPairs) {
         for (unsigned b0 = 0; b0 < total_slots; b0 += 2 * kFusedThreads * kFusedBatch) {
             i64x2 v[kFusedBatch];
@@ -373,9 +375,26 @@ __global__ __launch_bounds__(kFusedThreads) void rows_fused_kernel(
             }
 #pragma unroll
             for (int i = 0; i < kFusedBatch; ++i) {
-                const unsigned sl = b0 + 2 * (i * kFusedThreads + threadIdx.x);
-                sweep_count(v[i][0], sl, lo, hi, E, pre, rest, tile_ids);
-                sweep_count(v[i][1], sl + 1, lo, hi, E, pre, rest, tile_ids);
+                // The wave's 128 slots [ws, ws + 128) lie before the tile,
+                // after it, inside it, or (at most twice per sweep) across one
+                // of its ends; only the last case is sorted per lane.
+                const unsigned ws = b0 + 2u * (i * kFusedThreads + wv * kWave);
+                const uint64_t e0 = static_cast<uint64_t>(v[i][0]), e1 = static_cast<uint64_t>(v[i][1]);
+                if (ws + 2 * kWave <= lo || ws >= hi) {
+                    int32_t* h = ws < lo ? pre : rest;
+                    if (e0 < uE) atomicAdd(&h[e0], 1);
+                    if (e1 < uE) atomicAdd(&h[e1], 1);
+                } else if (ws >= lo && ws + 2 * kWave <= hi) {
+                    if (e0 < uE) atomicAdd(&rest[e0], 1);
+                    if (e1 < uE) atomicAdd(&rest[e1], 1);
+                    const unsigned sl = b0 + 2 * (i * kFusedThreads + threadIdx.x) - lo;
+                    tile_ids[sl] = e0 < uE ? static_cast<int32_t>(e0) : -1;
+                    tile_ids[sl + 1] = e1 < uE ? static_cast<int32_t>(e1) : -1;
+                } else {
+                    const unsigned sl = b0 + 2 * (i * kFusedThreads + threadIdx.x);
+                    sweep_count(v[i][0], sl, lo, hi, E, pre, rest, tile_ids);
+                    sweep_count(v[i][1], sl + 1, lo, hi, E, pre, rest, tile_ids);
+                }
             }
         }
     } else {
