@@ -160,6 +160,21 @@ def test_ht_edge_shapes(T, k, E, R, H):
     run_case(x, idx, None, E, R)
 
 
+# The multi-launch index: tile histograms summed by kHtRowsThreads / R
+# threads per rank, kHtHistLoads tiles each per round trip, so 64 ranks
+# over more than 128 tiles take two rounds; 33-64 ranks rank in two chunks
+# of at most 32; top-64 records take two batches of slot loads.
+@pytest.mark.parametrize("T,k,E,R", [(20000, 4, 128, 64), (17000, 3, 99, 33), (2100, 64, 128, 64),
+                                     (16500, 1, 17, 17)])
+def test_ht_multi_launch_index(T, k, E, R):
+    rng = np.random.default_rng(T + R)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int64)
+    idx[rng.random((T, k)) < 0.05] = -1
+    x = rng.integers(0, 0x7F00, size=(T, 16)).astype(np.uint16)
+    w = rng.random((T, k)).astype(np.float32)
+    run_case(x, idx, w, E, R)
+
+
 @pytest.mark.parametrize("T,k,E,R", [(200, 6, 24, 6), (3000, 8, 64, 8), (3001, 7, 64, 8),
                                      (5000, 6, 64, 32)])
 def test_ht_ids_with_high_word_set(T, k, E, R):
