@@ -127,7 +127,7 @@ def test_ht_parity_full_size(name):
 
 
 # One-launch index path (T <= 16384, R <= 16, k <= 16; top-k <= 8 and 9..16
-# instantiations) and the three-launch path beyond it, both sides of each limit.
+# instantiations) and the two-launch index path beyond it, both sides of each limit.
 # One-launch small-batch path (T * k <= 2048, T <= 512), including 64 ranks, a
 # ragged column segment and the limits on either side.
 @pytest.mark.parametrize("T,k,E,R,H", [(1, 8, 64, 64, 1024), (30, 8, 128, 64, 1032), (256, 8, 256, 16, 136),
@@ -180,7 +180,7 @@ def test_ht_multi_launch_index(T, k, E, R):
 def test_ht_ids_with_high_word_set(T, k, E, R):
     """Ids outside [0, E) whose low 32-bit word is a valid expert are empty
     slots, on the small-batch, one-launch (paired and single id loads) and
-    three-launch index paths."""
+    two-launch index paths."""
     rng = np.random.default_rng(T * k)
     idx = rng.integers(0, E, size=(T, k)).astype(np.int64)
     bad = rng.random((T, k)) < 0.15

@@ -14,7 +14,7 @@ Checks, phase by phase (each phase frees its buffers before the next):
 - combine (identity experts, num_rows = filled rows) on 256 sampled tokens,
   bit-exact against the oracle's fp32 chain over the same rows;
 - FP8 dispatch on 64 sampled tokens' rows against the oracle's cast;
-- rank-deduplicated dispatch (three-launch index path): maps equal to the
+- rank-deduplicated dispatch (two-launch index path): maps equal to the
   oracle's, every row equal to its token, its combine on sampled tokens;
 - padded layout at the mean expert load (so slots are dropped): counts and
   slot map equal to the oracle's, every filled slot equal to its token.
