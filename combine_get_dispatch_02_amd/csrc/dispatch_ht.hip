@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kHtRowsThreads) void ht_rows_kernel(
         // The slots' ids and weights are loaded kHtRecBatch at a time (the
         // tile's slots are contiguous; indices clamped, not branched on), so
         // one round trip serves kHtRecBatch slots.
-        const uint64_t chunk = nr == 64 ? ~uint64_t(0) : ((uint64_t(1) << nr) - 1);
+        const uint64_t chunk = (uint64_t(1) << nr) - 1;            // nr <= 32
         const int ns = nt * k;
         const int64_t s0 = t0 * k;
         for (int i0 = tid; i0 < ns; i0 += kHtRowsThreads * kHtRecBatch) {
