@@ -564,8 +564,9 @@ hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const floa
     if (T <= kHtFusedMaxTokens && R <= kHtFusedMaxR && k <= kHtFusedMaxK) {
         const int ntiles = static_cast<int>(ceil_div(T, kHtFusedTile));
         const int64_t x_bytes = T * static_cast<int64_t>(H) * 2;
-        const int64_t pf_bytes = x_bytes < kPrefetchMaxBytes ? x_bytes : kPrefetchMaxBytes;
-        const int pf_blocks = prefetch_blocks(pf_bytes);
+        const int64_t pf_bytes = !prefetch_pays(x_bytes, false) ? 0
+                                 : x_bytes < kPrefetchMaxBytes ? x_bytes : kPrefetchMaxBytes;
+        const int pf_blocks = pf_bytes > 0 ? prefetch_blocks(pf_bytes) : 0;
         const bool pairs = k % 2 == 0 && (reinterpret_cast<uintptr_t>(topk_idx) & 15u) == 0;
         auto kern = k <= 8 ? (pairs ? ht_fused_kernel<8, 1, true> : ht_fused_kernel<8, 1, false>)
                            : (pairs ? ht_fused_kernel<16, 1, true> : ht_fused_kernel<16, 1, false>);

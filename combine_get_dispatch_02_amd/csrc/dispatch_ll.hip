@@ -49,10 +49,11 @@ hipError_t launch_dispatch_ll(const void* x, const int64_t* topk_idx, const floa
                                           recv_src_idx, recv_w, nullptr, nullptr, recv_count,
                                           token_slot, stream);
     }
+    const int64_t x_bytes = T * static_cast<int64_t>(H) * 2;
     const hipError_t e = launch_dispatch_index(topk_idx, topk_weights, T, k, E, 1, recv_src_idx,
-                                               recv_w, nullptr, nullptr, token_slot, workspace, x,
-                                               T * static_cast<int64_t>(H) * 2, cap, recv_count,
-                                               stream);
+                                               recv_w, nullptr, nullptr, token_slot, workspace,
+                                               prefetch_pays(x_bytes, !fp8) ? x : nullptr, x_bytes,
+                                               cap, recv_count, stream);
     if (e != hipSuccess) return e;
     const int64_t rows = static_cast<int64_t>(E) * cap;
     if (fp8)

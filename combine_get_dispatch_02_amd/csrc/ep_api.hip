@@ -92,10 +92,12 @@ int dispatch_bf16(const char* fn, const void* x, const int64_t* topk_idx, const 
                                                          recv_x, recv_src_idx, recv_w, expert_offset,
                                                          rank_offset, nullptr, token_row, st),
                           fn);
+    const int64_t x_bytes = T * static_cast<int64_t>(H) * 2;
     int s = hip_status(ep::launch_dispatch_index(topk_idx, topk_weights, T, k, E, R, recv_src_idx,
                                                  recv_w, expert_offset, rank_offset, token_row,
-                                                 workspace, x, T * static_cast<int64_t>(H) * 2, 0,
-                                                 nullptr, st),
+                                                 workspace,
+                                                 ep::prefetch_pays(x_bytes, true) ? x : nullptr,
+                                                 x_bytes, 0, nullptr, st),
                        fn);
     if (s != EP_OK) return s;
     return hip_status(ep::launch_dispatch_copy_bf16(x, token_row, recv_x, T * k, T, H, k, st), fn);
@@ -271,12 +273,13 @@ int ep_dispatch_fp8(const void* x, const int64_t* topk_idx, const float* topk_we
                                                         recv_expert_offset, recv_rank_offset,
                                                         nullptr, token_row, st),
                           fn);
+    const int64_t x_bytes = num_tokens * static_cast<int64_t>(hidden) * 2;
     s = hip_status(ep::launch_dispatch_index(topk_idx, topk_weights, num_tokens, num_topk,
                                              num_experts, num_ranks, recv_src_idx,
                                              recv_topk_weights, recv_expert_offset,
-                                             recv_rank_offset, token_row, workspace, x,
-                                             num_tokens * static_cast<int64_t>(hidden) * 2, 0,
-                                             nullptr, st),
+                                             recv_rank_offset, token_row, workspace,
+                                             ep::prefetch_pays(x_bytes, false) ? x : nullptr,
+                                             x_bytes, 0, nullptr, st),
                    fn);
     if (s != EP_OK) return s;
     return hip_status(ep::launch_dispatch_copy_fp8(x, token_row, recv_x_fp8, recv_scales,

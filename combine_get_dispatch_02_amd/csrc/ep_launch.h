@@ -36,6 +36,19 @@ constexpr int64_t kSmallSlots = 2048;
 // inside the 256 MB Infinity Cache), for the copy that follows.
 constexpr int kPrefetchBlocks = 192;
 constexpr int64_t kPrefetchMaxBytes = int64_t(64) << 20;
+// The prefetch pays only while it covers most of x, and less so the more the
+// copy writes per byte of x it reads (index + copy, kernel trace, caches
+// evicted first, top-8 of 256 experts unless noted).  bf16 copy: -4 us with
+// 58.7 MB of x, -8 us with 67 MB (top-6 of 64), but +3.7 / +8 / +14 us with
+// 117 / 176 / 470 MB; FP8 copy: -4.7 us at 58.7 MB, -2 us at 117 MB, none
+// at 470 MB; the rank-deduplicated copy (5.3 rows per token): -13 us at
+// 117 MB, none at 235 MB.  So up to kPrefetchMaxXBf16 bytes of x for the
+// bf16 copy and kPrefetchMaxXOther for the FP8 and rank-deduplicated ones.
+constexpr int64_t kPrefetchMaxXBf16 = int64_t(80) << 20;
+constexpr int64_t kPrefetchMaxXOther = int64_t(128) << 20;
+inline bool prefetch_pays(int64_t x_bytes, bool bf16_fanout) {
+    return x_bytes <= (bf16_fanout ? kPrefetchMaxXBf16 : kPrefetchMaxXOther);
+}
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
