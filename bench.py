@@ -661,7 +661,7 @@ def main():
                               "x read from HBM)", "bound": "hbm", "achieved": round(q_gbs, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(q_gbs / HBM_PEAK_GBS, 4),
                     "alg_bytes_per_launch": int(B["dispatch_fp8_cached"]), "avg_launch_us": round(q_us, 2)}
-    roofline = {"kernel": "combine_kernel<2, 8, true> (ep_combine)", "bound": "hbm",
+    roofline = {"kernel": "combine_kernel<1, true> (ep_combine)", "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "alg_bytes_per_launch": int(B["combine"]), "avg_launch_us": round(c_us, 2),
