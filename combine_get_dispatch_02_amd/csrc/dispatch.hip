@@ -457,16 +457,20 @@ __device__ __forceinline__ int64_t wave_index() {
            __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
 }
 
-// bf16 copy: one block per (token t, column segment of kCopyVec*64 16-byte
-// vectors = 2 KB), one wave per destination row.  The block has
-// kb = min(k, 8) waves; wave w writes rows j = w, w + kb, ... of the token.
-// Every wave loads the same segment of x[t] with plain (cached) loads, so the
-// kb waves of the block (same CU, same XCD) share it through L2 and HBM reads
-// it once; each lane then issues kCopyVec 16-byte non-temporal stores per
-// row.  On MI355X this drains a 1:k fan-out faster than one wave storing one
-// load to all k rows (measured: ~6% at 4096 x 7168, k = 8); longer runs per
-// wave (4 or 7 vectors per lane) were markedly slower.  (kCopyVec = 2.)
-
+// bf16 copy: one block per (token t, column segment of CV*64 16-byte vectors,
+// CV KB), one wave per destination row.  The block has kb = min(k, 8) waves;
+// wave w writes rows j = w, w + kb, ... of the token.  Every wave loads the
+// same segment of x[t] with plain (cached) loads, so the kb waves of the
+// block (same CU, same XCD) share it through L2 and HBM reads it once; each
+// lane then issues CV 16-byte non-temporal stores per row.  On MI355X this
+// drains a 1:k fan-out faster than one wave storing one load to all k rows
+// (measured: ~6% at 4096 x 7168, k = 8); longer runs per wave (4 or 7
+// vectors per lane) were markedly slower.  CV = 2 (kCopyVec) reads x from
+// HBM best; CV = 1 is faster once the index launch has read x into the
+// Infinity Cache (at 4096 x 7168, top-8: 87.6 against 89.7 us, kernel trace,
+// three alternating pairs) but much slower from HBM (133 against 96 us), and
+// slower for the rank-deduplicated copy either way.
+template <int CV>
 __global__ __launch_bounds__(512) void copy_bf16_kernel(const u32x4* __restrict__ x,
                                                         const int32_t* __restrict__ token_row,
                                                         u32x4* __restrict__ recv, int64_t num_rows,
@@ -475,29 +479,29 @@ __global__ __launch_bounds__(512) void copy_bf16_kernel(const u32x4* __restrict_
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int64_t t = blockIdx.x / segs;
     const int seg = static_cast<int>(blockIdx.x - t * segs);
-    const int v0 = seg * (kCopyVec * kWave) + lane;
+    const int v0 = seg * (CV * kWave) + lane;
     // The wave's first destination row (w < kb <= k) is requested together
     // with x, so the two round trips overlap.
     const int r0 = token_row[t * k + w];
-    u32x4 val[kCopyVec];
+    u32x4 val[CV];
 #pragma unroll
-    for (int u = 0; u < kCopyVec; ++u) {
+    for (int u = 0; u < CV; ++u) {
         const int v = v0 + u * kWave;
         if (v < V) val[u] = x[t * V + v];
     }
     // A segment wholly inside the row is stored without a per-lane guard: a
     // branch around each store made the compiler wait for the previous store
     // to complete before issuing the next.
-    const bool full = (seg + 1) * (kCopyVec * kWave) <= V;
+    const bool full = (seg + 1) * (CV * kWave) <= V;
     auto store_row = [&](int r) {
         if (r < 0 || r >= num_rows) return;
         u32x4* dst = recv + static_cast<int64_t>(r) * V;
         if (full) {
 #pragma unroll
-            for (int u = 0; u < kCopyVec; ++u) __builtin_nontemporal_store(val[u], dst + v0 + u * kWave);
+            for (int u = 0; u < CV; ++u) __builtin_nontemporal_store(val[u], dst + v0 + u * kWave);
         } else {
 #pragma unroll
-            for (int u = 0; u < kCopyVec; ++u) {
+            for (int u = 0; u < CV; ++u) {
                 const int v = v0 + u * kWave;
                 if (v < V) __builtin_nontemporal_store(val[u], dst + v);
             }
@@ -928,14 +932,21 @@ hipError_t launch_dispatch_small_fp8(const void* x, const int64_t* topk_idx,
 
 hipError_t launch_dispatch_copy_bf16(const void* x, const int32_t* token_row, void* recv_x,
                                      int64_t num_rows, int64_t T, int H, int k,
-                                     hipStream_t stream) {
+                                     hipStream_t stream, bool x_cached) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
-    const int segs = static_cast<int>(ceil_div(V, kCopyVec * kWave));
     const int kb = k < 8 ? k : 8;
-    hipLaunchKernelGGL(copy_bf16_kernel, dim3(static_cast<unsigned>(T * segs)), dim3(kb * kWave), 0,
-                       stream, static_cast<const u32x4*>(x), token_row, static_cast<u32x4*>(recv_x),
-                       num_rows, V, k, kb, segs);
+    const int64_t segs1 = ceil_div(V, kWave);
+    if (x_cached && T * segs1 * kb * kWave <= kMaxLaunchThreads) {
+        hipLaunchKernelGGL(copy_bf16_kernel<1>, dim3(static_cast<unsigned>(T * segs1)), dim3(kb * kWave),
+                           0, stream, static_cast<const u32x4*>(x), token_row,
+                           static_cast<u32x4*>(recv_x), num_rows, V, k, kb, static_cast<int>(segs1));
+        return hipGetLastError();
+    }
+    const int segs = static_cast<int>(ceil_div(V, kCopyVec * kWave));
+    hipLaunchKernelGGL(copy_bf16_kernel<kCopyVec>, dim3(static_cast<unsigned>(T * segs)),
+                       dim3(kb * kWave), 0, stream, static_cast<const u32x4*>(x), token_row,
+                       static_cast<u32x4*>(recv_x), num_rows, V, k, kb, segs);
     return hipGetLastError();
 }
 

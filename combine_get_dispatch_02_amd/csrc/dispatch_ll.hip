@@ -59,7 +59,8 @@ hipError_t launch_dispatch_ll(const void* x, const int64_t* topk_idx, const floa
     if (fp8)
         return launch_dispatch_copy_fp8(x, token_slot, static_cast<uint8_t*>(recv_q_or_x), recv_scales,
                                         rows, T, H, k, stream);
-    return launch_dispatch_copy_bf16(x, token_slot, recv_q_or_x, rows, T, H, k, stream);
+    return launch_dispatch_copy_bf16(x, token_slot, recv_q_or_x, rows, T, H, k, stream,
+                                     prefetch_pays(x_bytes, true));
 }
 
 }  // namespace ep

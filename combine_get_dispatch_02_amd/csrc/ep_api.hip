@@ -100,7 +100,9 @@ int dispatch_bf16(const char* fn, const void* x, const int64_t* topk_idx, const 
                                                  x_bytes, 0, nullptr, st),
                        fn);
     if (s != EP_OK) return s;
-    return hip_status(ep::launch_dispatch_copy_bf16(x, token_row, recv_x, T * k, T, H, k, st), fn);
+    return hip_status(ep::launch_dispatch_copy_bf16(x, token_row, recv_x, T * k, T, H, k, st,
+                                                    ep::prefetch_pays(x_bytes, true)),
+                      fn);
 }
 
 // ---- fixed device scratch of ep_dispatch_noalloc ------------------------------
