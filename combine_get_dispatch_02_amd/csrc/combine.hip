@@ -66,13 +66,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
             for (int jj = 0; jj < KB; ++jj) {
                 const int j = j0 + jj;
                 rows[jj] = j < k ? read_lane(my_row, j) : -1;
-                // Every row's load is issued unconditionally, so all KB rows
-                // are in flight before any is waited on (a branch or select
-                // around each row's load makes the compiler wait for it
-                // before the next).  An empty slot reads row 0 of y -- or,
-                // when y has no rows, the wave's own output segment, which
-                // only this wave writes, after its loads -- and never
-                // accumulates it.
+                // One row at a time: an empty slot (a wave-uniform test) is
+                // skipped, no load.  Several rows: every row's load is issued
+                // unconditionally, so all KB rows are in flight before any is
+                // waited on (a branch or select around each row's load makes
+                // the compiler wait for it before the next); an empty slot
+                // reads row 0 of y -- or, when y has no rows, the wave's own
+                // output segment, which only this wave writes, after its
+                // loads -- and never accumulates it.
+                if (KB == 1 && rows[jj] < 0) continue;
                 const u32x4* src = num_rows > 0 ? y + static_cast<int64_t>(rows[jj] >= 0 ? rows[jj] : 0) * V
                                                 : out + t * V;
                 val[jj] = __builtin_nontemporal_load(src + vc);
