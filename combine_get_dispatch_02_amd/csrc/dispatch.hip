@@ -512,45 +512,15 @@ __global__ __launch_bounds__(512) void copy_bf16_kernel(const u32x4* __restrict_
     for (int j = w + kb; j < k; j += kb) store_row(token_row[t * k + j]);
 }
 
-// Quantise the 16 consecutive bf16 channels a lane holds (two 16-byte
-// vectors) as part of a 128-channel block shared by 8 aligned lanes: block
-// amax by three xor-shuffles, scale = amax / 448 (one correctly rounded fp32
+// Quantise the 8 consecutive bf16 channels a lane holds (one 16-byte vector)
+// as part of a 128-channel block shared by 16 aligned lanes: block amax by
+// four xor-shuffles, scale = amax / 448 (one correctly rounded fp32
 // division), codes = E4M3FN(x / scale), or all zero when the scale is 0.
 // amax is the largest magnitude that is not NaN: magnitudes are compared as
 // integers (the order of non-negative floats, +inf included), with NaN bit
 // patterns counted as 0, so the result does not depend on how a float max
 // treats quiet or signalling NaNs.
 // Every lane of the wave must call it (the shuffles span the wave).
-__device__ __forceinline__ u32x4 quantize16(u32x4 a0, u32x4 a1, float& scale) {
-    float f[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[2 * i] = bf16_lo(a0[i]);
-        f[2 * i + 1] = bf16_hi(a0[i]);
-        f[8 + 2 * i] = bf16_lo(a1[i]);
-        f[8 + 2 * i + 1] = bf16_hi(a1[i]);
-    }
-    uint32_t amax = 0u;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const uint32_t m = __float_as_uint(f[i]) & 0x7FFFFFFFu;
-        amax = max(amax, m > 0x7F800000u ? 0u : m);
-    }
-    amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 1, kWave)));
-    amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 2, kWave)));
-    amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 4, kWave)));
-    const float s = __uint_as_float(amax) / 448.0f;
-    u32x4 q = {0u, 0u, 0u, 0u};
-    if (s > 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) q[i / 4] |= e4m3fn_encode(f[i] / s) << (8 * (i % 4));
-    }
-    scale = s;
-    return q;
-}
-
-// The same for the 8 channels of one 16-byte vector, 16 aligned lanes per
-// 128-channel block (four xor-shuffles).
 __device__ __forceinline__ u32x2 quantize8(u32x4 a, float& scale) {
     float f[8];
 #pragma unroll
@@ -800,9 +770,10 @@ __global__ __launch_bounds__(512) void dispatch_small_bf16_kernel(
     }
 }
 
-// FP8, small batches: block = 4 waves = (token, 4096-channel segment), each
-// wave quantises 1024 channels and stores them to every row of the token.
-__global__ __launch_bounds__(256) void dispatch_small_fp8_kernel(
+// FP8, small batches: block = 8 waves = (token, 4096-channel segment), each
+// wave quantises 512 channels (as copy_fp8) and stores them to every row of
+// the token.
+__global__ __launch_bounds__(512) void dispatch_small_fp8_kernel(
     const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
     const float* __restrict__ topk_weights, int64_t T, int k, int E, int R, int cap, int H,
     int segs, uint8_t* __restrict__ recv_q, float* __restrict__ recv_scales,
@@ -817,25 +788,21 @@ __global__ __launch_bounds__(256) void dispatch_small_fp8_kernel(
     const int seg = static_cast<int>(blockIdx.x - t * segs);
     const int V = H / 8;
     const int nb = H / 128;
-    const int ch0 = seg * 4096 + w * 1024 + lane * 16;
+    const int ch0 = seg * 4096 + w * 512 + lane * 8;
     const bool active = ch0 < H;
-    u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
-    if (active) {
-        const u32x4* src = x + t * V + ch0 / 8;
-        a0 = __builtin_nontemporal_load(src);
-        a1 = __builtin_nontemporal_load(src + 1);
-    }
+    u32x4 a = {0u, 0u, 0u, 0u};
+    if (active) a = __builtin_nontemporal_load(x + t * V + ch0 / 8);
     small_token_rows(topk_idx, topk_weights, T, k, E, R, cap, t, seg == 0, blockIdx.x == 0,
                      token_row, recv_src_idx, recv_w, expert_offset, rank_offset, recv_count, lds,
                      rows);
     float s;
-    const u32x4 q = quantize16(a0, a1, s);
+    const u32x2 q = quantize8(a, s);
     if (!active) return;
     for (int j = 0; j < k; ++j) {
         const int r = rows[j];
         if (r < 0) continue;
-        __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(recv_q + static_cast<int64_t>(r) * H + ch0));
-        if ((lane & 7) == 0) recv_scales[static_cast<int64_t>(r) * nb + ch0 / 128] = s;
+        __builtin_nontemporal_store(q, reinterpret_cast<u32x2*>(recv_q + static_cast<int64_t>(r) * H + ch0));
+        if ((lane & 15) == 0) recv_scales[static_cast<int64_t>(r) * nb + ch0 / 128] = s;
     }
 }
 
@@ -952,7 +919,7 @@ hipError_t launch_dispatch_small_fp8(const void* x, const int64_t* topk_idx,
                                      int32_t* recv_count, int32_t* token_row,
                                      hipStream_t stream) {
     const int segs = static_cast<int>(ceil_div(H, 4096));
-    hipLaunchKernelGGL(dispatch_small_fp8_kernel, dim3(static_cast<unsigned>(T * segs)), dim3(256),
+    hipLaunchKernelGGL(dispatch_small_fp8_kernel, dim3(static_cast<unsigned>(T * segs)), dim3(512),
                        small_lds_bytes(E), stream, static_cast<const u32x4*>(x), topk_idx,
                        (recv_w ? topk_weights : nullptr), T, k, E, R, cap, H, segs, recv_q,
                        recv_scales, token_row, recv_src_idx, (topk_weights ? recv_w : nullptr),
