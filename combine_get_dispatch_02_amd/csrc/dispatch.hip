@@ -929,10 +929,10 @@ hipError_t launch_dispatch_small_fp8(const void* x, const int64_t* topk_idx,
 
 hipError_t launch_dispatch_copy_bf16(const void* x, const int32_t* token_row, void* recv_x,
                                      int64_t num_rows, int64_t T, int H, int k,
-                                     hipStream_t stream, bool x_cached) {
+                                     hipStream_t stream, bool x_cached, int max_waves) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
-    const int kb = k < 8 ? k : 8;
+    const int kb = k < max_waves ? k : max_waves;
     const int64_t segs1 = ceil_div(V, kWave);
     if (x_cached && T * segs1 * kb * kWave <= kMaxLaunchThreads) {
         hipLaunchKernelGGL(copy_bf16_kernel<1>, dim3(static_cast<unsigned>(T * segs1)), dim3(kb * kWave),

@@ -529,6 +529,13 @@ __global__ __launch_bounds__(kHtSmallThreads) void ht_small_kernel(
     }
 }
 
+// Waves per block of the rank-deduplicated copy.  A token reaches few of R
+// ranks, so most of its R slots are empty; beyond 8 ranks, 4 waves that each
+// walk R/4 slots beat 8 that each walk R/8: at 32768 tokens over 32 ranks
+// the copy takes 686 against 743 us (1 or 2 waves: 786 / 742 us; 16: 1052
+// us), while at 8 ranks 4 and 8 waves are within 0.5 us (kernel trace).
+inline int ht_copy_waves(int R) { return R > 8 ? 4 : 8; }
+
 __global__ void ht_zero_offsets_kernel(int32_t* rank_offset, int R) {
     if (static_cast<int>(threadIdx.x) <= R) rank_offset[threadIdx.x] = 0;
 }
@@ -576,7 +583,8 @@ hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const floa
                            pf_bytes / 16, static_cast<uint32_t*>(workspace));
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        return launch_dispatch_copy_bf16(x, token_rank_row, recv_x, T * R, T, H, R, stream);
+        return launch_dispatch_copy_bf16(x, token_rank_row, recv_x, T * R, T, H, R, stream, false,
+                                         ht_copy_waves(R));
     }
     const int ntiles = static_cast<int>(ceil_div(T, kHtTile));
     int32_t* hist = static_cast<int32_t*>(workspace);
@@ -587,7 +595,8 @@ hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const floa
                        hist, token_rank_row, rank_offset, recv_src_idx, recv_topk_idx, recv_w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_dispatch_copy_bf16(x, token_rank_row, recv_x, T * R, T, H, R, stream);
+    return launch_dispatch_copy_bf16(x, token_rank_row, recv_x, T * R, T, H, R, stream, false,
+                                     ht_copy_waves(R));
 }
 
 }  // namespace ep

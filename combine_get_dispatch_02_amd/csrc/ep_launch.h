@@ -130,10 +130,11 @@ hipError_t launch_dispatch_ll(const void* x, const int64_t* topk_idx, const floa
 // Copy kernels: every slot whose row lies in [0, num_rows) receives x[t]
 // (bf16) or its FP8 cast; other slots are skipped.  x_cached: x was just read
 // through the caches by the index launch (its prefetch), which the bf16 copy
-// then reads in 1 KB instead of 2 KB segments.
+// then reads in 1 KB instead of 2 KB segments.  max_waves (<= 8): waves per
+// bf16 copy block, each taking every max_waves-th of a token's k slots.
 hipError_t launch_dispatch_copy_bf16(const void* x, const int32_t* token_row, void* recv_x,
                                      int64_t num_rows, int64_t T, int H, int k,
-                                     hipStream_t stream, bool x_cached = false);
+                                     hipStream_t stream, bool x_cached = false, int max_waves = 8);
 hipError_t launch_dispatch_copy_fp8(const void* x, const int32_t* token_row, uint8_t* recv_q,
                                     float* recv_scales, int64_t num_rows, int64_t T, int H, int k,
                                     hipStream_t stream);
