@@ -89,7 +89,9 @@ bool dispatch_is_small(int64_t T, int k);
 // copies cannot, and their callers reject shapes beyond it.
 constexpr int64_t kMaxLaunchThreads = 0xFFFFFFFFll;
 // 16-byte vectors per lane per destination row in the bf16 copies (2 KB of a
-// row per wave); copy_launch_fits assumes it.
+// row per wave) when x comes from HBM; copy_launch_fits checks that shape
+// (the 1 KB form used once x is cached falls back to it when its twice as
+// many blocks would not fit one launch).
 constexpr int kCopyVec = 2;
 bool copy_launch_fits(int64_t T, int H, int fanout);
 // cap == 0: packed receive order (expert_offset / rank_offset written);
