@@ -15,8 +15,8 @@
 // per-rank rows.  That case has its own instantiation, which loads no weights
 // and adds (acc + y rounds exactly as fma(1, y, acc) does).
 //
-// Large batches read one row at a time per wave (KB = 1), small ones all
-// rows at once (KB = 8).  Bound by the DRAM side of the scattered row reads,
+// Large batches (at least 6144 tiles) read one row at a time per wave
+// (KB = 1), small ones all rows at once (KB = 8).  Bound by the DRAM side of the scattered row reads,
 // large batches gain from many small waves each with one row in flight: at
 // 4096 tokens x 7168, top-8 of 256 experts the kernel takes 89.3 us with 1 KB
 // tiles and one row per wave, against 90.4 us with 2 KB tiles and one row
@@ -128,8 +128,10 @@ hipError_t launch_combine(const void* expert_out, int64_t num_rows, const int32_
                           hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int V = H / 8;
-    // Large: at least 8192 1 KB tiles (4096 x 7168 has 57344).
-    const bool large = T * ceil_div(V, kWave) >= 8192;
+    // Large: at least 6144 1 KB tiles (4096 x 7168 has 57344).  At H = 7168,
+    // top-8 the one-row form is 1.4 us slower at 256 tokens (3584 tiles) and
+    // 0.5 us faster at 512 (7168 tiles) than the all-rows one.
+    const bool large = T * ceil_div(V, kWave) >= 6144;
     if (topk_weights)
         return large ? launch_kb<1, true>(expert_out, num_rows, token_row, topk_weights, out, T, V, k, stream)
                      : launch_kb<8, true>(expert_out, num_rows, token_row, topk_weights, out, T, V, k, stream);

@@ -545,15 +545,15 @@ def test_combine_bit_exact_fma_chain(name):
         np.testing.assert_array_equal(got, ref_c)
 
 
-@pytest.mark.parametrize("T,H", [(5, 8), (600, 1032), (4095, 1024), (4096, 1024)],
+@pytest.mark.parametrize("T,H", [(5, 8), (600, 1032), (3071, 1024), (3072, 1024)],
                          ids=["golden", "all-rows", "all-rows-last", "row-at-a-time-first"])
 def test_combine_order_golden(T, H):
     """The hand-worked cases of tests/golden/combine_order.json (their answers
     change with the slot order, the fusion and the grouping of the sum),
-    repeated over T tokens and H channels.  Batches of at least 8192 1 KB
+    repeated over T tokens and H channels.  Batches of at least 6144 1 KB
     column tiles take the combine form that reads one row at a time (the
     full-size batches' form), smaller ones the form with all rows in flight:
-    4095 x 1024 (8190 tiles) is the largest of the one, 4096 x 1024 the
+    3071 x 1024 (6142 tiles) is the largest of the one, 3072 x 1024 the
     smallest of the other."""
     from test_oracle_combine import _load_order_golden
     y, trow, w, exp_bits, _, H0 = _load_order_golden()
