@@ -32,9 +32,11 @@
 namespace ep {
 namespace {
 
-constexpr int kIndexWaves = kIndexThreads / kWave;
+constexpr int kHistThreads = 256;    // tile_hist block
+constexpr int kHistSlotsPerLane = kMaxTileSlots / kHistThreads;
 constexpr int kHistBatch = 64;
-constexpr int kSlotsPerLane = kMaxTileSlots / kIndexThreads;
+// LDS budget of the ranking launch of the two-launch receive order.
+constexpr size_t kRankMaxLds = 48 * 1024;
 // Fused receive-order kernel: every block histograms all T*k slots itself.
 constexpr int kFusedThreads = 1024;
 // Loads per thread per sweep step.  8 measured ~1 us faster per ep_dispatch
@@ -53,39 +55,39 @@ typedef long long i64x2 __attribute__((ext_vector_type(2)));
 // routed to e (LDS atomics; integer sums do not depend on order).
 // Blocks past the tiles (if any) read part of x through the caches instead
 // (see prefetch_vectors).
-__global__ __launch_bounds__(kIndexThreads) void tile_hist_kernel(
+__global__ __launch_bounds__(kHistThreads) void tile_hist_kernel(
     const int64_t* __restrict__ topk_idx, int64_t T, int k, int E, int tile_tokens,
     int32_t* __restrict__ hist, int ntiles, const u32x4* __restrict__ pf_src, int64_t pf_vecs,
     uint32_t* __restrict__ pf_sink) {
     if (static_cast<int>(blockIdx.x) >= ntiles) {   // whole block: x prefetch only
-        prefetch_vectors<kIndexThreads>(pf_src, pf_vecs, static_cast<int>(blockIdx.x) - ntiles,
-                                        static_cast<int>(gridDim.x) - ntiles, pf_sink);
+        prefetch_vectors<kHistThreads>(pf_src, pf_vecs, static_cast<int>(blockIdx.x) - ntiles,
+                                       static_cast<int>(gridDim.x) - ntiles, pf_sink);
         return;
     }
     extern __shared__ int32_t h[];
-    for (int e = threadIdx.x; e < E; e += kIndexThreads) h[e] = 0;
+    for (int e = threadIdx.x; e < E; e += kHistThreads) h[e] = 0;
     __syncthreads();
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tile_tokens;
     const int nt = static_cast<int>(T - t0 < tile_tokens ? T - t0 : tile_tokens);
-    const int S = nt * k;                 // <= kMaxTileSlots = kSlotsPerLane * kIndexThreads
+    const int S = nt * k;                 // <= kMaxTileSlots = kHistSlotsPerLane * kHistThreads
     const int64_t* ids = topk_idx + t0 * k;
     // All of a thread's ids are requested before any is counted (indices
     // clamped to the tile's last slot: no branch around a load, which would
     // make the compiler wait for each in turn).
-    int64_t v[kSlotsPerLane];
+    int64_t v[kHistSlotsPerLane];
 #pragma unroll
-    for (int i = 0; i < kSlotsPerLane; ++i) {
-        const int s = i * kIndexThreads + static_cast<int>(threadIdx.x);
+    for (int i = 0; i < kHistSlotsPerLane; ++i) {
+        const int s = i * kHistThreads + static_cast<int>(threadIdx.x);
         v[i] = ids[s < S ? s : S - 1];
     }
 #pragma unroll
-    for (int i = 0; i < kSlotsPerLane; ++i) {
-        const int s = i * kIndexThreads + static_cast<int>(threadIdx.x);
+    for (int i = 0; i < kHistSlotsPerLane; ++i) {
+        const int s = i * kHistThreads + static_cast<int>(threadIdx.x);
         if (s < S && v[i] >= 0 && v[i] < E) atomicAdd(&h[v[i]], 1);
     }
     __syncthreads();
     int32_t* out = hist + static_cast<int64_t>(blockIdx.x) * E;
-    for (int e = threadIdx.x; e < E; e += kIndexThreads) out[e] = h[e];
+    for (int e = threadIdx.x; e < E; e += kHistThreads) out[e] = h[e];
 }
 
 // In-place exclusive scan of a[0..n) held in LDS by a block of NT threads,
@@ -125,19 +127,21 @@ __device__ int block_exclusive_scan(int32_t* a, int n, int32_t* wave_tot) {
     return total;
 }
 
-// The tile's slots are ranked by the block's first kIndexWaves waves: wave w
-// owns slots [w*Q, (w+1)*Q) (Q a multiple of 64), lane l of it the slots
-// w*Q + 64*i + l, whose raw ids and weights it loads into registers here.
+// The tile's slots are ranked by the block's first NR threads (NR / 64
+// waves; NR is chosen per launch, see index_rankers): wave w owns slots
+// [w*Q, (w+1)*Q) (Q a multiple of 64), lane l of it the slots w*Q + 64*i + l,
+// whose raw ids and weights it loads into registers here.
+template <int NR>
 __device__ __forceinline__ void load_tile_slots(const int64_t* __restrict__ topk_idx,
                                                 const float* __restrict__ topk_weights,
                                                 bool want_w, int64_t s0, int S, int Q,
-                                                int64_t (&raw)[kSlotsPerLane],
-                                                float (&wt)[kSlotsPerLane]) {
+                                                int64_t (&raw)[kMaxTileSlots / NR],
+                                                float (&wt)[kMaxTileSlots / NR]) {
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
-    const bool ranker = threadIdx.x < kIndexThreads;
+    const bool ranker = threadIdx.x < NR;
 #pragma unroll
-    for (int i = 0; i < kSlotsPerLane; ++i) {
+    for (int i = 0; i < kMaxTileSlots / NR; ++i) {
         const int s = wave * Q + i * kWave + lane;
         const bool in = ranker && i * kWave < Q && s < S;
         raw[i] = in ? topk_idx[s0 + s] : -1;
@@ -155,27 +159,29 @@ __device__ __forceinline__ void load_tile_slots(const int64_t* __restrict__ topk
 // holds positions within expert e instead of rows, and a slot's row becomes
 // e*cap + position, or -1 from position cap on.  Called by every thread of the
 // block.
-__device__ __forceinline__ void rank_tile(const int (&ids)[kSlotsPerLane],
-                                          const float (&wt)[kSlotsPerLane], const int32_t* base,
+template <int NR>
+__device__ __forceinline__ void rank_tile(const int (&ids)[kMaxTileSlots / NR],
+                                          const float (&wt)[kMaxTileSlots / NR], const int32_t* base,
                                           int32_t* wc, int E, int S, int Q, int64_t s0, int64_t t0,
                                           int k, int nbits, int32_t* __restrict__ token_row,
                                           int32_t* __restrict__ recv_src_idx,
                                           float* __restrict__ recv_w, int cap) {
+    constexpr int kRankWaves = NR / kWave;
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
-    const bool ranker = threadIdx.x < kIndexThreads;
-    for (int i = threadIdx.x; i < kIndexWaves * E; i += blockDim.x) wc[i] = 0;
+    const bool ranker = threadIdx.x < NR;
+    for (int i = threadIdx.x; i < kRankWaves * E; i += blockDim.x) wc[i] = 0;
     __syncthreads();
     int32_t* my = wc + (ranker ? wave : 0) * E;
     if (ranker) {
 #pragma unroll
-        for (int i = 0; i < kSlotsPerLane; ++i)
+        for (int i = 0; i < kMaxTileSlots / NR; ++i)
             if (ids[i] >= 0) atomicAdd(&my[ids[i]], 1);
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         int run = base[e];
-        for (int w = 0; w < kIndexWaves; ++w) {
+        for (int w = 0; w < kRankWaves; ++w) {
             const int v = wc[w * E + e];
             wc[w * E + e] = run;
             run += v;
@@ -184,7 +190,7 @@ __device__ __forceinline__ void rank_tile(const int (&ids)[kSlotsPerLane],
     __syncthreads();
     if (!ranker) return;
 #pragma unroll
-    for (int i = 0; i < kSlotsPerLane; ++i) {
+    for (int i = 0; i < kMaxTileSlots / NR; ++i) {
         if (i * kWave >= Q) break;
         const int s = wave * Q + i * kWave + lane;
         const bool in = s < S;
@@ -218,9 +224,10 @@ __device__ __forceinline__ void write_offsets(const int32_t* eoff, int total, in
 
 // Two-kernel path, second kernel: one block per tile.  Per expert, the tile
 // histograms of all tiles (-> expert offsets) and of the tiles before this
-// one (-> this tile's base rows).  LDS: base[E], wc[kIndexWaves][E],
-// wave_tot[kIndexWaves].
-__global__ __launch_bounds__(kIndexThreads) void rows_kernel(
+// one (-> this tile's base rows).  Blocks of NR threads, all of them
+// ranking.  LDS: base[E], wc[NR/64][E], wave_tot[NR/64].
+template <int NR>
+__global__ __launch_bounds__(NR) void rows_kernel(
     const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int64_t T,
     int k, int E, int R, int tile_tokens, int ntiles, int nbits, const int32_t* __restrict__ hist,
     int32_t* __restrict__ token_row, int32_t* __restrict__ recv_src_idx,
@@ -228,27 +235,28 @@ __global__ __launch_bounds__(kIndexThreads) void rows_kernel(
     int32_t* __restrict__ rank_offset, int cap, int32_t* __restrict__ recv_count,
     const u32x4* __restrict__ pf_src, int64_t pf_vecs, uint32_t* __restrict__ pf_sink) {
     if (static_cast<int>(blockIdx.x) >= ntiles) {   // whole block: x prefetch only
-        prefetch_vectors<kIndexThreads>(pf_src, pf_vecs, static_cast<int>(blockIdx.x) - ntiles,
-                                        static_cast<int>(gridDim.x) - ntiles, pf_sink);
+        prefetch_vectors<NR>(pf_src, pf_vecs, static_cast<int>(blockIdx.x) - ntiles,
+                             static_cast<int>(gridDim.x) - ntiles, pf_sink);
         return;
     }
+    constexpr int kLane = kMaxTileSlots / NR;      // slots per ranking lane
     extern __shared__ int32_t lds[];
     int32_t* base = lds;
     int32_t* wc = lds + E;
-    int32_t* wave_tot = lds + (1 + kIndexWaves) * E;
+    int32_t* wave_tot = lds + (1 + NR / kWave) * E;
     const int c = blockIdx.x;
     const int64_t t0 = static_cast<int64_t>(c) * tile_tokens;
     const int nt = static_cast<int>(T - t0 < tile_tokens ? T - t0 : tile_tokens);
     const int S = nt * k;
     const int64_t s0 = t0 * k;
-    const int Q = (S + kIndexThreads - 1) / kIndexThreads * kWave;
+    const int Q = (S + NR - 1) / NR * kWave;
 
-    int64_t raw[kSlotsPerLane];
-    float wt[kSlotsPerLane];
-    load_tile_slots(topk_idx, topk_weights, recv_w != nullptr, s0, S, Q, raw, wt);
+    int64_t raw[kLane];
+    float wt[kLane];
+    load_tile_slots<NR>(topk_idx, topk_weights, recv_w != nullptr, s0, S, Q, raw, wt);
     // The histograms were written by blocks on every XCD, so most come from
     // beyond this XCD's L2: issue them kHistBatch at a time.
-    for (int e = threadIdx.x; e < E; e += kIndexThreads) {
+    for (int e = threadIdx.x; e < E; e += NR) {
         int tot = 0, pre = 0;
         for (int c0 = 0; c0 < ntiles; c0 += kHistBatch) {
             int v[kHistBatch];
@@ -264,23 +272,23 @@ __global__ __launch_bounds__(kIndexThreads) void rows_kernel(
         base[e] = tot;
         wc[e] = pre;
     }
-    int ids[kSlotsPerLane];
+    int ids[kLane];
 #pragma unroll
-    for (int i = 0; i < kSlotsPerLane; ++i)
+    for (int i = 0; i < kLane; ++i)
         ids[i] = (raw[i] >= 0 && raw[i] < E) ? static_cast<int>(raw[i]) : -1;
     __syncthreads();
     if (cap > 0) {        // padded layout: counts, and positions within each expert
-        for (int e = threadIdx.x; e < E; e += kIndexThreads) {
+        for (int e = threadIdx.x; e < E; e += NR) {
             if (c == 0) recv_count[e] = min(base[e], cap);
             base[e] = wc[e];
         }
     } else {
-        const int total = block_exclusive_scan<kIndexThreads>(base, E, wave_tot);
+        const int total = block_exclusive_scan<NR>(base, E, wave_tot);
         if (c == 0) write_offsets(base, total, E, R, expert_offset, rank_offset);
-        for (int e = threadIdx.x; e < E; e += kIndexThreads) base[e] += wc[e];
+        for (int e = threadIdx.x; e < E; e += NR) base[e] += wc[e];
     }
     __syncthreads();
-    rank_tile(ids, wt, base, wc, E, S, Q, s0, t0, k, nbits, token_row, recv_src_idx, recv_w, cap);
+    rank_tile<NR>(ids, wt, base, wc, E, S, Q, s0, t0, k, nbits, token_row, recv_src_idx, recv_w, cap);
 }
 
 // Fused path (one launch): one block of kFusedThreads per tile.  Every block
@@ -292,7 +300,8 @@ __global__ __launch_bounds__(kIndexThreads) void rows_kernel(
 // trip costs microseconds here, so the kernel makes exactly one: the tile's
 // weights are requested first, the sweep's loads next, and the threads that
 // load the tile's own ids keep them in LDS for the ranking.
-// LDS: pre[E], rest[E], wc[kIndexWaves][E], wave_tot[kFusedThreads/64],
+// The first NR threads rank the tile.
+// LDS: pre[E], rest[E], wc[NR/64][E], wave_tot[kFusedThreads/64],
 //      tile_ids[tile slots], tile_w[tile slots].
 // The launch carries extra blocks past the tiles that read the first
 // pf_vecs 16-byte vectors of x once through the caches while the tile blocks
@@ -311,8 +320,8 @@ __device__ __forceinline__ void sweep_count(int64_t v, unsigned sl, unsigned lo,
 }
 
 // kPairs: topk_idx is 16-byte aligned and each load brings two consecutive
-// ids (slots 2p, 2p+1).
-template <bool kPairs>
+// ids (slots 2p, 2p+1).  NR <= kFusedThreads: the ranking threads.
+template <bool kPairs, int NR>
 __global__ __launch_bounds__(kFusedThreads) void rows_fused_kernel(
     const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int64_t T,
     int k, int E, int R, int tile_tokens, int nbits, int32_t* __restrict__ token_row,
@@ -329,7 +338,7 @@ __global__ __launch_bounds__(kFusedThreads) void rows_fused_kernel(
     int32_t* pre = lds;
     int32_t* rest = lds + E;
     int32_t* wc = lds + 2 * E;
-    int32_t* wave_tot = lds + (2 + kIndexWaves) * E;
+    int32_t* wave_tot = lds + (2 + NR / kWave) * E;
     int32_t* tile_ids = wave_tot + kFusedThreads / kWave;
     float* tile_w = reinterpret_cast<float*>(tile_ids + tile_tokens * k);
     const int c = blockIdx.x;
@@ -337,7 +346,7 @@ __global__ __launch_bounds__(kFusedThreads) void rows_fused_kernel(
     const int nt = static_cast<int>(T - t0 < tile_tokens ? T - t0 : tile_tokens);
     const int S = nt * k;
     const int64_t s0 = t0 * k;
-    const int Q = (S + kIndexThreads - 1) / kIndexThreads * kWave;
+    const int Q = (S + NR - 1) / NR * kWave;
     const bool want_w = recv_w != nullptr;
 
     // The tile's weights: requested before the sweep so both share one round trip.
@@ -428,14 +437,14 @@ __global__ __launch_bounds__(kFusedThreads) void rows_fused_kernel(
         for (int e = threadIdx.x; e < E; e += kFusedThreads) pre[e] += rest[e];
     }
     // The ranking waves pick up their slots from LDS.
-    int ids[kSlotsPerLane];
-    float wt[kSlotsPerLane];
+    int ids[kMaxTileSlots / NR];
+    float wt[kMaxTileSlots / NR];
     {
         const int lane = lane_id();
         const int wave = threadIdx.x / kWave;
-        const bool ranker = threadIdx.x < kIndexThreads;
+        const bool ranker = threadIdx.x < NR;
 #pragma unroll
-        for (int i = 0; i < kSlotsPerLane; ++i) {
+        for (int i = 0; i < kMaxTileSlots / NR; ++i) {
             const int s = wave * Q + i * kWave + lane;
             const bool in = ranker && i * kWave < Q && s < S;
             ids[i] = in ? tile_ids[s] : -1;
@@ -443,7 +452,7 @@ __global__ __launch_bounds__(kFusedThreads) void rows_fused_kernel(
         }
     }
     __syncthreads();
-    rank_tile(ids, wt, pre, wc, E, S, Q, s0, t0, k, nbits, token_row, recv_src_idx, recv_w, cap);
+    rank_tile<NR>(ids, wt, pre, wc, E, S, Q, s0, t0, k, nbits, token_row, recv_src_idx, recv_w, cap);
 }
 
 __global__ void zero_offsets_kernel(int32_t* expert_offset, int E, int32_t* rank_offset, int R) {
@@ -808,6 +817,21 @@ __global__ __launch_bounds__(512) void dispatch_small_fp8_kernel(
 
 }  // namespace
 
+// Ranking threads per tile block of the receive-order kernels.  Each ranking
+// wave walks its share of the tile 64 slots at a time, one dependent LDS
+// update per step, so more waves per tile finish sooner: at 32768 x top-8 of
+// 256 experts (64 tiles of 4096 slots) the ranking launch takes 21.6 us with
+// 256 threads, 15.0 with 512 and 13.5 with 1024; the one-launch receive order
+// at 4096 x top-8 12.1 us with 256 and 11.2 with 512 or 1024 (kernel trace,
+// no x prefetch).  Every ranking wave keeps a counter per expert in LDS, so
+// NR is the largest of 1024, 512 and 256 for which those counters and the
+// kernel's other fixed_ints words fit the budget.
+static int index_rankers(size_t fixed_ints, int E, size_t budget) {
+    for (int nr = 1024; nr > 256; nr /= 2)
+        if ((fixed_ints + static_cast<size_t>(nr / kWave) * E) * sizeof(int32_t) <= budget) return nr;
+    return 256;
+}
+
 // Tokens per tile of the receive-order kernels: a multiple of 64, at least 64,
 // large enough that there are at most kMaxTiles tiles (each tile sums the
 // histograms of the tiles before it), and small enough that a tile's ids fit
@@ -846,15 +870,18 @@ hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weig
     float* w_out = topk_weights ? recv_w : nullptr;
     const int64_t pf_bytes = x ? (x_bytes < kPrefetchMaxBytes ? x_bytes : kPrefetchMaxBytes) : 0;
     uint32_t* pf_sink = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + index_hist_bytes(T, k, E));
-    const size_t fused_lds = (static_cast<size_t>(2 + kIndexWaves) * E + kFusedThreads / kWave +
-                              2 * static_cast<size_t>(tt) * k) * sizeof(int32_t);
+    const size_t fused_fixed = 2 * static_cast<size_t>(E) + kFusedThreads / kWave + 2 * static_cast<size_t>(tt) * k;
+    const int fused_nr = index_rankers(fused_fixed, E, kFusedMaxLds);
+    const size_t fused_lds = (fused_fixed + static_cast<size_t>(fused_nr / kWave) * E) * sizeof(int32_t);
     if (T * k <= kFusedMaxSlots && fused_lds <= kFusedMaxLds) {
         const size_t lds = fused_lds;
         // Prefetch blocks only while that part of x fits the cache comfortably.
         const int pf_blocks = pf_bytes > 0 ? prefetch_blocks(pf_bytes) : 0;
         const bool pairs = (reinterpret_cast<uintptr_t>(topk_idx) & 15u) == 0;
-        hipLaunchKernelGGL(pairs ? rows_fused_kernel<true> : rows_fused_kernel<false>,
-                           dim3(ntiles + pf_blocks), dim3(kFusedThreads), lds, stream,
+        auto kern = fused_nr == 1024 ? (pairs ? rows_fused_kernel<true, 1024> : rows_fused_kernel<false, 1024>)
+                  : fused_nr == 512  ? (pairs ? rows_fused_kernel<true, 512> : rows_fused_kernel<false, 512>)
+                                     : (pairs ? rows_fused_kernel<true, 256> : rows_fused_kernel<false, 256>);
+        hipLaunchKernelGGL(kern, dim3(ntiles + pf_blocks), dim3(kFusedThreads), lds, stream,
                            topk_idx, w_in, T, k, E, R, tt, nbits, token_row, recv_src_idx, w_out,
                            expert_offset, rank_offset, ntiles, cap, recv_count,
                            static_cast<const u32x4*>(x), pf_bytes / 16, pf_sink);
@@ -867,16 +894,18 @@ hipError_t launch_dispatch_index(const int64_t* topk_idx, const float* topk_weig
     // tiles of up to 4096 slots of its own and all of it goes with the
     // ranking launch (at 32768 x top-8 the split measured 3 us slower).
     const int64_t pf_a = T * k <= kSplitPrefetchSlots ? (pf_bytes / 2) / 16 * 16 : 0;
-    const int pf_blocks_a = pf_a > 0 ? 4 * prefetch_blocks(pf_a) : 0;
-    hipLaunchKernelGGL(tile_hist_kernel, dim3(ntiles + pf_blocks_a), dim3(kIndexThreads),
+    const int pf_blocks_a = pf_a > 0 ? (1024 / kHistThreads) * prefetch_blocks(pf_a) : 0;
+    hipLaunchKernelGGL(tile_hist_kernel, dim3(ntiles + pf_blocks_a), dim3(kHistThreads),
                        static_cast<size_t>(E) * sizeof(int32_t), stream, topk_idx, T, k, E, tt, hist,
                        ntiles, static_cast<const u32x4*>(x), pf_a / 16, pf_sink);
-    const size_t lds = (static_cast<size_t>(1 + kIndexWaves) * E + kIndexWaves) * sizeof(int32_t);
-    // The ranking launch carries the rest of the x prefetch (in 256-thread blocks).
+    const int nr = index_rankers(static_cast<size_t>(E) + kFusedThreads / kWave, E, kRankMaxLds);
+    const size_t lds = (static_cast<size_t>(1 + nr / kWave) * E + nr / kWave) * sizeof(int32_t);
+    // The ranking launch carries the rest of the x prefetch (in blocks of nr threads).
     const int64_t pf_b = pf_bytes - pf_a;
-    const int pf_blocks = pf_b > 0 ? 4 * prefetch_blocks(pf_b) : 0;
+    const int pf_blocks = pf_b > 0 ? (1024 / nr) * prefetch_blocks(pf_b) : 0;
     const u32x4* pf_src_b = pf_b > 0 ? reinterpret_cast<const u32x4*>(static_cast<const char*>(x) + pf_a) : nullptr;
-    hipLaunchKernelGGL(rows_kernel, dim3(ntiles + pf_blocks), dim3(kIndexThreads), lds, stream, topk_idx,
+    auto rows = nr == 1024 ? rows_kernel<1024> : nr == 512 ? rows_kernel<512> : rows_kernel<256>;
+    hipLaunchKernelGGL(rows, dim3(ntiles + pf_blocks), dim3(nr), lds, stream, topk_idx,
                        w_in, T, k, E, R, tt, ntiles, nbits, hist, token_row, recv_src_idx, w_out,
                        expert_offset, rank_offset, cap, recv_count, pf_src_b, pf_b / 16, pf_sink);
     return hipGetLastError();

@@ -17,7 +17,6 @@ constexpr int kLayoutTokensPerBlock = 256;
 // with wave ballots, and tiles are chained by per-expert prefix sums.
 constexpr int kMaxTiles = 64;
 constexpr int kMaxTileSlots = 4096;
-constexpr int kIndexThreads = 256;
 // Up to this many slots (T*k) one fused launch computes the receive order;
 // beyond it, a histogram launch feeds the ranking launch.  Every fused block
 // sweeps all T*k ids, so its cost grows with the batch: measured on MI355X
