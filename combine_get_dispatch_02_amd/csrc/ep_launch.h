@@ -20,12 +20,11 @@ constexpr int kMaxTileSlots = 4096;
 // Up to this many slots (T*k) one fused launch computes the receive order;
 // beyond it, a histogram launch feeds the ranking launch.  Every fused block
 // sweeps all T*k ids, so its cost grows with the batch: measured on MI355X
-// with the x prefetch on both paths (kernel trace, top-8 of 256 experts), the
-// fused launch takes 18.9 / 20.9 / 26.0 us at 49152 / 65536 / 98304 slots
-// against 20.3 / 20.8 / 22.4 us for the two launches (18.2 against 18.3 us
-// at 8192 x top-6 of 64), and the two launches are 27 us faster at 262144
-// (one ep_dispatch of 32768 x 7168, top-8).
-constexpr int64_t kFusedMaxSlots = int64_t(1) << 16;
+// (kernel trace, top-8 of 256 experts, no x prefetch, as at hidden 7168 from
+// 6144 tokens on), the fused launch takes 13.8 / 15.9 / 20.6 us at
+// 49152 / 65536 / 98304 slots against 4.8 + 9.4 / 4.8 + 9.4 / 4.8 + 10.5 us
+// for the two launches (12.9 against 4.8 + 8.5 us at 8192 x top-6 of 64).
+constexpr int64_t kFusedMaxSlots = int64_t(3) << 14;
 constexpr size_t kFusedMaxLds = 64 * 1024;
 // Up to this many slots (T*k) each copy block derives its own token's rows and
 // ep_dispatch / ep_dispatch_fp8 are a single launch.

@@ -98,7 +98,7 @@ def test_ll_parity_oracle_sized(case, fp8):
 
 @pytest.mark.parametrize("T,k,E,cap,H", [(40000, 8, 256, 200, 16), (33000, 8, 64, 4000, 16)])
 def test_ll_two_kernel_index_path(T, k, E, cap, H):
-    """T*k > 2^16: the packed rows come from the two-launch receive-order path."""
+    """T*k > 49152: the packed rows come from the two-launch receive-order path."""
     print(f"[ll-big] T={T} k={k} E={E} cap={cap} H={H}", flush=True)
     rng = np.random.default_rng(T)
     idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int64)

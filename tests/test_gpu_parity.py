@@ -302,7 +302,7 @@ def test_edge_duplicates_and_out_of_range_ids():
 
 # Ids outside [0, E) whose low 32-bit word is a valid expert (2^32 + e, a
 # negative value with low word e): empty slots like -1, on the single-launch
-# (T*k <= 2048), fused (<= 2^16 slots) and two-launch receive-order paths.
+# (T*k <= 2048), fused (<= 49152 slots) and two-launch receive-order paths.
 HIGH_WORD_IDS = [2 ** 32, 2 ** 32 + 3, -(2 ** 32), 2 ** 40 + 1, -(2 ** 63) + 2, 2 ** 62 + 5]
 
 
@@ -455,7 +455,7 @@ def test_edge_non_finite_tokens(T, k):
 
 
 @pytest.mark.parametrize("T,k,E,R,H,mask,ids_off", [
-    (40000, 8, 256, 8, 64, 0.0, 0),      # T*k > 2^16: histogram launch + ranking launch
+    (40000, 8, 256, 8, 64, 0.0, 0),      # T*k > 49152: histogram launch + ranking launch
     (33000, 8, 64, 8, 64, 0.05, 0),      # same path, masked slots, ragged last tile
     (3000, 6, 2048, 64, 128, 0.02, 0),   # many experts and ranks (fused path, large LDS)
     (20000, 16, 2048, 64, 16, 0.0, 0),   # many experts, two launches, k > 8
@@ -463,13 +463,15 @@ def test_edge_non_finite_tokens(T, k):
     (4096, 8, 256, 8, 64, 0.03, 1),      # same, ids only 8-byte aligned (one id per load)
     (3001, 7, 256, 8, 64, 0.02, 0),      # odd T*k: the last id pair holds one id
     (3001, 7, 256, 8, 64, 0.02, 1),      # odd T*k, ids only 8-byte aligned
-    (8192, 6, 64, 8, 64, 0.02, 0),       # fused, 49152 slots over 64 experts
-    (8192, 8, 256, 8, 64, 0.03, 0),      # T*k = 2^16: the last fused size
-    (8192, 8, 256, 8, 64, 0.03, 1),      # same, ids only 8-byte aligned
-    (8193, 8, 256, 8, 64, 0.03, 0),      # one token more: two launches
+    (8192, 6, 64, 8, 64, 0.02, 0),       # T*k = 49152 over 64 experts: the last fused size
+    (8193, 6, 64, 8, 64, 0.02, 0),       # one token more: two launches
+    (6144, 8, 256, 8, 64, 0.03, 1),      # fused, 49152 slots, ids only 8-byte aligned
+    (8192, 8, 256, 8, 64, 0.03, 0),      # T*k = 2^16: two launches
+    (3000, 8, 1024, 32, 64, 0.02, 0),    # 1024 experts: 512 ranking threads (fused)
+    (9000, 8, 1024, 32, 64, 0.02, 0),    # same, two launches
 ])
 def test_parity_receive_order_paths(T, k, E, R, H, mask, ids_off):
-    """Both receive-order paths (one fused launch up to 2^16 slots, two
+    """Both receive-order paths (one fused launch up to 49152 slots, two
     launches above; both carry the x prefetch) against the oracle, element by
     element.  ids_off = 1 places topk_idx one int64 into a device buffer, so
     the fused sweep cannot read ids in 16-byte pairs."""
