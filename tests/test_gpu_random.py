@@ -7,7 +7,7 @@ dispatch, FP8 dispatch, cached dispatch, rank-deduplicated dispatch, the
 padded layout (bf16 and FP8) and the combines over each map: maps and bytes
 bit-exact, FP8 codes within one step (scales bit-exact), combines bit-exact.
 The shapes cross the kernels' internal limits: the one-launch small batch
-(T*k <= 2048), the one-launch receive order (<= 2^15 slots) and beyond, the
+(T*k <= 2048), the one-launch receive order (<= 49152 slots) and beyond, the
 one-launch rank-deduplicated index (R, k <= 16) and beyond.  A second,
 wider draw reaches top-64, 2048 experts, 64 ranks and 40000 tokens.
 """
