@@ -9,8 +9,8 @@
 //
 // Up to 2048 slots (T * k) and 512 tokens: one launch (ht_small, index and
 // copy per (token, segment) block, as the packed small-batch dispatch).
-// Up to 16384 tokens, 16 ranks and top-16: two launches, deterministic, no
-// global atomics:
+// Up to 8192 tokens, 16 ranks, top-16 and 65536 (token, rank) pairs: two
+// launches, deterministic, no global atomics:
 //   ht_fused      one block of 1024 threads per 64-token tile: every block
 //                 sweeps all tokens (one token per thread per step), builds
 //                 each token's rank mask from an LDS table of rank bits, and
@@ -31,7 +31,8 @@
 //                 from one ballot per rank per wave; writes token_rank_row and
 //                 each row's source token and remapped top-k ids and weights
 //                 (one thread per (token, slot): the k threads of a token
-//                 store each row's k entries together)
+//                 store each row's k entries together); extra blocks read x
+//                 through the caches meanwhile, as in ht_fused
 //   copy          the bf16 copy kernel of ep_dispatch, driven by the [T, R]
 //                 map token_rank_row instead of the [T, k] token_row
 #include "../../include/ep.h"
@@ -81,7 +82,8 @@ constexpr int kHtStagePitch = kHtStageRanks + 1;
 constexpr int kHtHistLoads = 16;      // tile histogram entries per thread per round trip
 constexpr int kHtRecBatch = 8;        // slots whose ids a thread loads per round trip
 // Second launch of the multi-launch path: one block of kHtRowsThreads
-// threads per tile of kHtTile tokens, thread t < kHtTile owning token t.
+// threads per tile of kHtTile tokens, thread t < kHtTile owning token t,
+// then the x-prefetch blocks (if any).
 //   1. Per rank: its tokens in all tiles (-> recv_rank_offset) and in the
 //      tiles before this one, summed from the per-tile histograms by
 //      kHtRowsThreads / R threads per rank (kHtHistLoads loads each per round
@@ -106,7 +108,13 @@ __global__ __launch_bounds__(kHtRowsThreads) void ht_rows_kernel(
     int E, int R, uint32_t magic, uint32_t kmagic, int ntiles, const int32_t* __restrict__ hist,
     int32_t* __restrict__ token_rank_row, int32_t* __restrict__ rank_offset,
     int32_t* __restrict__ recv_src_idx, int64_t* __restrict__ recv_topk_idx,
-    float* __restrict__ recv_w) {
+    float* __restrict__ recv_w, const u32x4* __restrict__ pf_src, int64_t pf_vecs,
+    uint32_t* __restrict__ pf_sink) {
+    if (static_cast<int>(blockIdx.x) >= ntiles) {   // whole block: x prefetch only
+        prefetch_vectors<kHtRowsThreads>(pf_src, pf_vecs, static_cast<int>(blockIdx.x) - ntiles,
+                                         static_cast<int>(gridDim.x) - ntiles, pf_sink);
+        return;
+    }
     __shared__ int32_t wcnt[kHtWaves][EP_MAX_RANKS];       // per-wave counts -> first rows
     __shared__ int32_t part_tot[kHtRowsThreads], part_pre[kHtRowsThreads];
     __shared__ uint64_t tok_mask[kHtTile];
@@ -254,7 +262,17 @@ constexpr int kHtFusedWaves = kHtFusedThreads / kWave;
 constexpr int kHtFusedTile = kWave;                // tokens per tile: one ranking wave
 constexpr int kHtFusedMaxR = 16;
 constexpr int kHtFusedMaxK = 16;
-constexpr int64_t kHtFusedMaxTokens = 16384;
+// The fused sweep costs each block work in proportion to T (and to R), so
+// from some size on the two launches beat it, once the second of them also
+// carries the x prefetch (index + copy by kernel trace, top-8 of 256 experts,
+// ht_fused against ht_tile_hist + ht_rows): 69.4 against 70.4 us at 4096
+// tokens over 8 ranks, 139.4 against 139.2 at 8192 (57.8 against 57.9 at
+// 8192 x top-6 of 64), 104.4 against 99.3 at 8192 over 16 ranks (hidden
+// 4096), 224.9 against 217.4 at 12288 and 336.3 against 319.8 at 16384 over
+// 16 ranks (hidden 7168, no prefetch: x too large), 97.7 against 79.6 at
+// 16384 over 8 ranks (hidden 2048).
+constexpr int64_t kHtFusedMaxTokens = 8192;
+constexpr int64_t kHtFusedMaxTokenRanks = 65536;
 
 // KMAX >= k slots per token; NQ tokens per thread per sweep step.  One token
 // per step is fastest on MI355X even where it takes four steps (4096
@@ -542,10 +560,15 @@ __global__ void ht_zero_offsets_kernel(int32_t* rank_offset, int R) {
 
 }  // namespace
 
-size_t ht_workspace_bytes(int64_t T, int R) {
+// The per-tile rank counts of the three-launch path, then 256 bytes where
+// the x-prefetch blocks store their folded words (ht_fused uses the first
+// 256 bytes for those).
+static size_t ht_hist_bytes(int64_t T, int R) {
     const size_t b = static_cast<size_t>(ceil_div(T, kHtTile)) * static_cast<size_t>(R) * sizeof(int32_t);
     return round_up(b > 0 ? b : 1, 256);
 }
+
+size_t ht_workspace_bytes(int64_t T, int R) { return ht_hist_bytes(T, R) + 256; }
 
 hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const float* topk_weights,
                               int64_t T, int H, int k, int E, int R, void* recv_x,
@@ -568,11 +591,12 @@ hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const floa
                            recv_topk_idx, recv_w, rank_offset);
         return hipGetLastError();
     }
-    if (T <= kHtFusedMaxTokens && R <= kHtFusedMaxR && k <= kHtFusedMaxK) {
+    const int64_t x_bytes = T * static_cast<int64_t>(H) * 2;
+    const int64_t pf_bytes = !prefetch_pays(x_bytes, false) ? 0
+                             : x_bytes < kPrefetchMaxBytes ? x_bytes : kPrefetchMaxBytes;
+    if (T <= kHtFusedMaxTokens && T * R <= kHtFusedMaxTokenRanks && R <= kHtFusedMaxR &&
+        k <= kHtFusedMaxK) {
         const int ntiles = static_cast<int>(ceil_div(T, kHtFusedTile));
-        const int64_t x_bytes = T * static_cast<int64_t>(H) * 2;
-        const int64_t pf_bytes = !prefetch_pays(x_bytes, false) ? 0
-                                 : x_bytes < kPrefetchMaxBytes ? x_bytes : kPrefetchMaxBytes;
         const int pf_blocks = pf_bytes > 0 ? prefetch_blocks(pf_bytes) : 0;
         const bool pairs = k % 2 == 0 && (reinterpret_cast<uintptr_t>(topk_idx) & 15u) == 0;
         auto kern = k <= 8 ? (pairs ? ht_fused_kernel<8, 1, true> : ht_fused_kernel<8, 1, false>)
@@ -590,9 +614,13 @@ hipError_t launch_dispatch_ht(const void* x, const int64_t* topk_idx, const floa
     int32_t* hist = static_cast<int32_t*>(workspace);
     hipLaunchKernelGGL(ht_tile_hist_kernel, dim3(ntiles), dim3(kHtTile), 0, stream, topk_idx, T, k,
                        E, R, magic, hist);
-    hipLaunchKernelGGL(ht_rows_kernel, dim3(ntiles), dim3(kHtRowsThreads), 0, stream, topk_idx,
+    // The x prefetch rides on the ranking launch, in blocks of kHtRowsThreads.
+    const int pf_blocks = pf_bytes > 0 ? (1024 / kHtRowsThreads) * prefetch_blocks(pf_bytes) : 0;
+    uint32_t* pf_sink = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + ht_hist_bytes(T, R));
+    hipLaunchKernelGGL(ht_rows_kernel, dim3(ntiles + pf_blocks), dim3(kHtRowsThreads), 0, stream, topk_idx,
                        (recv_w ? topk_weights : nullptr), T, k, E, R, magic, rank_magic(k), ntiles,
-                       hist, token_rank_row, rank_offset, recv_src_idx, recv_topk_idx, recv_w);
+                       hist, token_rank_row, rank_offset, recv_src_idx, recv_topk_idx, recv_w,
+                       static_cast<const u32x4*>(x), pf_bytes / 16, pf_sink);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_dispatch_copy_bf16(x, token_rank_row, recv_x, T * R, T, H, R, stream, false,

@@ -126,8 +126,9 @@ def test_ht_parity_full_size(name):
     assert_combine(got, oracle.combine(pool, sel_map, None), "pooled partial results")
 
 
-# One-launch index path (T <= 16384, R <= 16, k <= 16; top-k <= 8 and 9..16
-# instantiations) and the two-launch index path beyond it, both sides of each limit.
+# One-launch index path (T <= 8192, T*R <= 65536, R <= 16, k <= 16; top-k <= 8
+# and 9..16 instantiations) and the two-launch index path beyond it (with its x
+# prefetch), both sides of each limit.
 # One-launch small-batch path (T * k <= 2048, T <= 512), including 64 ranks, a
 # ragged column segment and the limits on either side.
 @pytest.mark.parametrize("T,k,E,R,H", [(1, 8, 64, 64, 1024), (30, 8, 128, 64, 1032), (256, 8, 256, 16, 136),
@@ -147,7 +148,8 @@ def test_ht_small_batch_path(T, k, E, R, H):
                                        (700, 8, 2048, 64, 16), (257, 16, 64, 64, 64),
                                        (300, 12, 48, 12, 128), (130, 16, 16, 16, 64),
                                        (200, 9, 34, 17, 64), (130, 17, 17, 1, 64),
-                                       (16384, 2, 64, 8, 16), (16385, 2, 64, 8, 16),
+                                       (8192, 2, 64, 8, 16), (8193, 2, 64, 8, 16),
+                                       (4096, 2, 64, 16, 16), (4097, 2, 64, 16, 16),
                                        (100, 64, 128, 8, 64), (90, 64, 2048, 64, 16)])
 def test_ht_edge_shapes(T, k, E, R, H):
     rng = np.random.default_rng(T * R)
