@@ -14,9 +14,12 @@
 //                sizes), per-expert slot counts (LDS atomics)
 //   rows         per tile: per-expert prefix over earlier tiles + block scan
 //                over experts -> tile base rows; each lane holds its slots'
-//                ids in registers; the stable rank of every slot inside the tile from wave64
-//                ballot matching; writes token_row, recv_src_idx,
-//                recv_topk_weights and the offsets
+//                ids in registers; the stable rank of every slot inside the
+//                tile from wave64 ballot matching, by up to 16 waves (as LDS
+//                allows); writes token_row, recv_src_idx, recv_topk_weights
+//                and the offsets
+//   rows_fused   tile_hist and rows in one launch (every block sweeps all
+//                ids), up to kFusedMaxSlots slots
 //   copy_bf16    one block per (token, 2 KB column segment; 1 KB when the
 //                index launch has read x into the Infinity Cache), one wave
 //                per destination row: x[t] shared through L2, one 16-byte
